@@ -1,0 +1,196 @@
+"""Throughput of the fused, chunked top-K KL loss (forward + backward) on one MI355X.
+
+One step = one kd_chunked_kl_fwd_bwd call over the whole batch (every chunk: forward
+GEMM + logsumexp, gather, loss, recomputed logits -> dz, sparse correction, dh and dW
+GEMMs) with inputs already resident in HBM.  Prints one JSON line.
+
+Default workload: N=32768 tokens, d=3072, V=128256, K=100, chunk 2048, bf16, packed
+sequences with each sequence's first token masked (synthetic, seeded).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+GEMM_CLASSES = ("fwd_gemm_lse", "bwd_gemm_dz", "dh_gemm", "dw_gemm")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=2, help="workload id (synth.CONFIGS)")
+    ap.add_argument("--N", type=int, default=None, help="override the token count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="token rows of the workload timed through the CPU oracle")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="skip per-kernel HIP-event timing inside the timed region")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kd_kernels.hip", "kd_api.hip", "kd_internal.h"):
+        with open(os.path.join(ROOT, "output_head_kl_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """Counter-derived HBM bytes per launch recorded under profiles/, if the kernels have
+    not changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, rows):
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    sel = synth.subset_rows(inp.cfg, inp.seed, rows)
+    sub = synth.take_rows(inp, sel)
+    h64, W64 = sub.h64(), sub.W64()
+    t0 = time.perf_counter()
+    oracle.forward_backward(h64, W64, sub.idx, sub.p, sub.mask, block_rows=128)
+    dt = time.perf_counter() - t0
+    return {"value": len(sel) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(sel)} seeded token rows of the same workload (full V and d), "
+                      f"float64 numpy, loss + dh + dW, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+              "multi-GPU path; see DESIGN.md for how the work would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import output_head_kl_amd as kd
+    import synth
+
+    overrides = {} if args.N is None else {"N": args.N}
+    t_gen = time.perf_counter()
+    inp = synth.make(args.config, **overrides)
+    cfg = inp.cfg
+    print(f"[bench] generated workload {cfg.name} N={cfg.N} d={cfg.d} V={cfg.V} K={cfg.K} "
+          f"chunk={cfg.chunk} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    dev = "cuda"
+    if cfg.dtype == "bf16":
+        h = torch.from_numpy(inp.h.view(np.int16)).to(dev).view(torch.bfloat16)
+        W = torch.from_numpy(inp.W.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        h, W = torch.from_numpy(inp.h).to(dev), torch.from_numpy(inp.W).to(dev)
+    idx = torch.from_numpy(inp.idx).to(dev)
+    p = torch.from_numpy(inp.p).to(dev)
+    mask = torch.from_numpy(inp.mask).to(dev)
+    dt_code = kd.KD_BF16 if cfg.dtype == "bf16" else kd.KD_F32
+    ws = torch.empty(kd.workspace_bytes(cfg.N, cfg.d, cfg.V, cfg.K, cfg.chunk, dt_code),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+    def step():
+        return kd.fwd_bwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws)
+
+    for _ in range(args.warmup):
+        out = step()
+        del out
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    prof = not args.no_profile
+    if prof:
+        kd.profile_read()          # discard anything recorded so far
+        kd.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if prof:
+        kd.profile_enable(False)
+        ktimes = kd.profile_read()
+    loss_val = float(out[0].item())
+    del out
+    peak_gib = torch.cuda.max_memory_allocated() / 2**30
+
+    ms = elapsed / args.steps * 1e3
+    tokens_per_s = cfg.N * args.steps / elapsed
+    flops_step = 8.0 * cfg.N * cfg.V * cfg.d          # z, recomputed z, dh, dW
+    tflops = flops_step / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    workload = f"fused_kl_fwd_bwd_N{cfg.N}_d{cfg.d}_V{cfg.V}_K{cfg.K}_chunk{cfg.chunk}_{cfg.dtype}"
+
+    roofline = None
+    kernels = {}
+    if prof:
+        for name, (tot, n) in ktimes.items():
+            if n:
+                kernels[name] = {"total_ms_per_step": tot / args.steps, "launches_per_step": n / args.steps,
+                                 "avg_ms": tot / n}
+        gem = {k: v for k, v in kernels.items() if k in GEMM_CLASSES}
+        if gem:
+            dom = max(gem, key=lambda k: gem[k]["total_ms_per_step"])
+            # every GEMM launch processes one chunk: 2 * rows * V * d flops (rows = chunk
+            # except for a partial last chunk, averaged here over the step)
+            flops_launch = 2.0 * cfg.N * cfg.V * cfg.d / gem[dom]["launches_per_step"]
+            achieved = flops_launch / (gem[dom]["avg_ms"] * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                        "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                        "traffic": traffic_for(dom, workload)}
+
+    res = {
+        "metric": "tokens/s + MFMA util, fused KL fwd+bwd, N=32K d=3072 V=128256 K=100",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload, "N": cfg.N, "d": cfg.d, "V": cfg.V, "K": cfg.K,
+                   "chunk": cfg.chunk, "mask": cfg.mask},
+        "tflops_8NVd": round(tflops, 1),
+        "frac_of_peak_8NVd": round(tflops / peak, 4),
+        "peak_mem_gib": round(peak_gib, 3),
+        "loss": loss_val,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

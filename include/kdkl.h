@@ -1,0 +1,131 @@
+/*
+ * kdkl.h -- fused, chunked top-K KL distillation loss on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the "fused chunked KL loss" of "Efficient Knowledge
+ * Distillation for LLMs: Offline Top-K Logits and a Fused Chunked KL Loss":
+ * the student's vocabulary output projection joined to the loss calculation,
+ * processed one sequence chunk at a time and recomputed during backpropagation
+ * so that the full tokens-by-vocabulary logit tensor is never stored
+ * (thorstenmeyerai.com article, TL;DR and infographic "Fuse and chunk" /
+ * "Recompute backward"; aimodeling.com article, "Second cut").  The teacher is
+ * a cache of its top-K tokens and their probabilities per position
+ * (aimodeling.com article, "First cut": top-100 probabilities per token).
+ *
+ * For tokens n = 0..N-1 with hidden state h[n,:] and teacher entries
+ * (idx[n,k], p[n,k]), k = 0..K-1:
+ *
+ *   z[n,v]   = sum_j h[n,j] * W[v,j]                    student logits
+ *   lse[n]   = log sum_v exp z[n,v]
+ *   l[n]     = sum_k p[n,k] * (log p[n,k] - (z[n,idx[n,k]] - lse[n]))   (0 log 0 = 0)
+ *   loss     = sum_n mask[n] * l[n] / count,   count = #{n : mask[n] != 0}
+ *
+ * and the closed-form gradient of the legiblepapers.com summary
+ * (Cross-Examination & FAQs, Q5: a dense M*softmax term minus the sparse teacher
+ * correction at the top-K support positions):
+ *
+ *   dz[n,v]  = (mask[n]/count) * (M[n]*softmax(z[n,:])[v] - sum_{k: idx[n,k]=v} p[n,k]),
+ *   M[n]     = sum_k p[n,k],   dh = dz @ W,   dW = dz^T @ h.
+ *
+ * p is used as given (no renormalisation; M may be below 1); there is no term
+ * for the teacher mass outside the top K; temperature is 1.  With count == 0
+ * the loss, dh and dW are all zero.
+ *
+ * Memory: every pointer argument is owned by the caller; the library never
+ * allocates or frees device memory.  Scratch space is a caller-provided device
+ * workspace whose size depends on min(chunk, N), d, V and K but not otherwise on
+ * N, so peak device memory is linear in N.
+ */
+#ifndef KDKL_H
+#define KDKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of h, W and dh. */
+typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
+
+/* Return codes. */
+typedef enum {
+  KD_OK = 0,
+  KD_E_ARG = 1,          /* null pointer, bad size or alignment; nothing enqueued     */
+  KD_E_INDEX = 2,        /* a teacher index outside [0,V), or a probability that is
+                            negative, NaN or infinite; no output written             */
+  KD_E_WORKSPACE = 3,    /* workspace smaller than kd_workspace_bytes(); nothing done */
+  KD_E_UNSUPPORTED = 4,  /* valid but unsupported shape (d not a multiple of 8, ...)  */
+  KD_E_HIP = 5           /* a HIP runtime call failed; outputs undefined              */
+} kd_status;
+
+/*
+ * kd_workspace_bytes -- device workspace needed by kd_chunked_kl_fwd_bwd.
+ *
+ * Same size arguments as the main call.  Writes the byte count to *bytes_out.
+ * Pure host computation (no GPU use).  Returns KD_OK, KD_E_ARG or
+ * KD_E_UNSUPPORTED under the same rules as kd_chunked_kl_fwd_bwd.
+ */
+int kd_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                       int32_t dtype, size_t *bytes_out);
+
+/*
+ * kd_chunked_kl_fwd_bwd -- loss, dL/dh and dL/dW in one call.
+ *
+ * Device pointers (all caller-owned, row-major, contiguous):
+ *   h         [N, d]  dtype           student hidden states (16-byte aligned)
+ *   W         [V, d]  dtype           output projection (16-byte aligned)
+ *   topk_idx  [N, K]  int32           teacher token indices
+ *   topk_p    [N, K]  float32         teacher probabilities
+ *   loss_mask [N]     uint8           nonzero = token counts; NULL = every token counts
+ *   loss      [1]     float32         mean loss over counted tokens (written)
+ *   dh        [N, d]  dtype           dL/dh, overwritten; rounded once to dtype (RNE)
+ *   dW        [V, d]  float32         dL/dW, overwritten (16-byte aligned)
+ *   row_loss  [N]     float32         optional: mask[n] ? l[n] : 0     (NULL = skip)
+ *   row_lse   [N]     float32         optional: lse[n]                 (NULL = skip)
+ *   zg        [N, K]  float32         optional: z[n, idx[n,k]]         (NULL = skip)
+ *   workspace         >= kd_workspace_bytes(...) bytes, 256-byte aligned
+ * Sizes: N >= 0, 1 <= K <= 65536, V >= 1, d >= 8 with d % 8 == 0, chunk >= 1,
+ *   N*d, V*d and N*K below 2^62.  N == 0 writes loss = 0 and dW = 0.
+ * chunk is the number of token rows whose logits are live at once; the last
+ *   chunk may be partial; results do not depend on it beyond float rounding.
+ * stream: a hipStream_t (NULL = the null stream).  All work is enqueued on it.
+ *   The call synchronises the stream once, after validating the teacher entries
+ *   and counting the mask; the rest is asynchronous and the outputs are ready when
+ *   the stream's work completes.  Calls sharing one workspace must not overlap.
+ * Errors: host-side checks run before any device work (KD_E_ARG,
+ *   KD_E_UNSUPPORTED, KD_E_WORKSPACE).  Invalid teacher entries give
+ *   KD_E_INDEX with no output written.  kd_last_error() describes the failure.
+ */
+int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype,
+                          const int32_t *topk_idx, const float *topk_p,
+                          const uint8_t *loss_mask,
+                          int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                          float *loss, void *dh, float *dW,
+                          float *row_loss, float *row_lse, float *zg,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Text describing the last non-OK return on the calling thread ("" if none). */
+const char *kd_last_error(void);
+
+/* Library interface version (increments on any change to this header). */
+int kd_version(void);
+
+/*
+ * Kernel timing for measurement.  While enabled, the library records a pair of
+ * HIP events on the call's stream around every launch and files it under the
+ * launch's kernel class.  kd_profile_read waits for the recorded events, adds
+ * their durations into *total_ms and *launches for the class, and clears them.
+ * Classes are numbered 0 .. kd_profile_num_classes()-1; kd_profile_class_name
+ * names them.  Not thread-safe; meant for benchmarks.
+ */
+int kd_profile_enable(int on);
+int kd_profile_num_classes(void);
+const char *kd_profile_class_name(int cls);
+int kd_profile_read(int cls, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDKL_H */

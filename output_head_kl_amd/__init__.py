@@ -1,0 +1,160 @@
+"""Fused, chunked top-K KL distillation loss on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libkdkl.so`` (C ABI in ``include/kdkl.h``).  Every
+step of the computation runs in the library's HIP kernels; this module only
+allocates outputs and the workspace with torch and passes pointers and the
+current HIP stream.  There is no fallback: if the library is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = ["KDError", "library_path", "workspace_bytes", "fwd_bwd", "profile_enable",
+           "profile_read", "profile_classes", "KD_F32", "KD_BF16"]
+
+KD_F32, KD_BF16 = 0, 1
+_STATUS = {0: "KD_OK", 1: "KD_E_ARG", 2: "KD_E_INDEX", 3: "KD_E_WORKSPACE",
+           4: "KD_E_UNSUPPORTED", 5: "KD_E_HIP"}
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdkl.so")
+
+
+class KDError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    lib.kd_workspace_bytes.argtypes = [i64, i64, i64, i32, i64, i32, ctypes.POINTER(sz)]
+    lib.kd_workspace_bytes.restype = ctypes.c_int
+    lib.kd_chunked_kl_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
+                                          vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_chunked_kl_fwd_bwd.restype = ctypes.c_int
+    lib.kd_last_error.argtypes = []
+    lib.kd_last_error.restype = ctypes.c_char_p
+    lib.kd_version.restype = ctypes.c_int
+    lib.kd_profile_enable.argtypes = [ctypes.c_int]
+    lib.kd_profile_num_classes.restype = ctypes.c_int
+    lib.kd_profile_class_name.argtypes = [ctypes.c_int]
+    lib.kd_profile_class_name.restype = ctypes.c_char_p
+    lib.kd_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64)]
+    _LIB = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise KDError(rc, _lib().kd_last_error().decode())
+
+
+def workspace_bytes(N: int, d: int, V: int, K: int, chunk: int, dtype: int = KD_BF16) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib().kd_workspace_bytes(N, d, V, K, chunk, dtype, ctypes.byref(out)))
+    return int(out.value)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KD_BF16
+    if t.dtype == torch.float32:
+        return KD_F32
+    raise TypeError(f"h and W must be bfloat16 or float32, not {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: bool = False,
+            workspace=None, stream=None):
+    """Mean top-K KL loss with its gradients, computed chunk by chunk on the GPU.
+
+    Args (torch CUDA tensors, contiguous):
+      h [N, d] and W [V, d]: bfloat16 or float32 (same dtype);
+      topk_idx [N, K] int32; topk_p [N, K] float32; loss_mask [N] uint8/bool or None.
+      chunk: token rows whose logits are live at once.
+      rows: also return per-row loss, logsumexp and the logits at the teacher's indices.
+      workspace: optional uint8 tensor of at least ``workspace_bytes(...)`` bytes.
+    Returns (loss[1] f32, dh [N, d] dtype, dW [V, d] f32) and, with ``rows``,
+    (row_loss [N], row_lse [N], zg [N, K]) as float32.
+    """
+    import torch
+    dt = _dtype_code(h)
+    if W.dtype != h.dtype:
+        raise TypeError("h and W must have the same dtype")
+    if topk_idx.dtype != torch.int32 or topk_p.dtype != torch.float32:
+        raise TypeError("topk_idx must be int32 and topk_p float32")
+    tensors = [h, W, topk_idx, topk_p] + ([loss_mask] if loss_mask is not None else [])
+    for t in tensors:
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    N, d = h.shape
+    V, d2 = W.shape
+    K = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
+    if d2 != d or tuple(topk_idx.shape) != (N, K) or tuple(topk_p.shape) != (N, K):
+        raise ValueError("shape mismatch among h, W, topk_idx and topk_p")
+    if loss_mask is not None:
+        if loss_mask.dtype == torch.bool:
+            loss_mask = loss_mask.view(torch.uint8)
+        if loss_mask.dtype != torch.uint8 or tuple(loss_mask.shape) != (N,):
+            raise ValueError("loss_mask must be uint8/bool of shape [N]")
+    dev = h.device
+    need = workspace_bytes(N, d, V, K, chunk, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    dh = torch.empty((N, d), dtype=h.dtype, device=dev)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    row_loss = row_lse = zg = None
+    if rows:
+        row_loss = torch.empty(N, dtype=torch.float32, device=dev)
+        row_lse = torch.empty(N, dtype=torch.float32, device=dev)
+        zg = torch.empty((N, K), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(_lib().kd_chunked_kl_fwd_bwd(
+        _ptr(h), _ptr(W), dt, _ptr(topk_idx), _ptr(topk_p), _ptr(loss_mask), N, d, V, K, chunk,
+        _ptr(loss), _ptr(dh), _ptr(dW), _ptr(row_loss), _ptr(row_lse), _ptr(zg),
+        _ptr(workspace), workspace.numel(), stream))
+    if rows:
+        return loss, dh, dW, row_loss, row_lse, zg
+    return loss, dh, dW
+
+
+def profile_enable(on: bool = True) -> None:
+    _check(_lib().kd_profile_enable(1 if on else 0))
+
+
+def profile_classes():
+    lib = _lib()
+    return [lib.kd_profile_class_name(i).decode() for i in range(lib.kd_profile_num_classes())]
+
+
+def profile_read():
+    """{class name: (total_ms, launches)} for launches since the last read (waits for them)."""
+    lib = _lib()
+    out = {}
+    for i, name in enumerate(profile_classes()):
+        ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+        _check(lib.kd_profile_read(i, ctypes.byref(ms), ctypes.byref(n)))
+        out[name] = (ms.value, n.value)
+    return out

@@ -1,0 +1,292 @@
+// C-ABI front end of the fused, chunked top-K KL loss (declared in include/kdkl.h).
+//
+// Host-side argument checks run before any HIP call, so a bad call never touches
+// the device.  The call then validates the teacher entries and counts the loss mask
+// on the device, synchronises the stream once to read the result, and enqueues the
+// per-chunk sequence: forward GEMM (per-tile max / sum-exp), gather at the teacher's
+// indices, logsumexp + loss, backward GEMM (recomputed logits -> dz), sparse
+// correction of dz, dh GEMM + reduction, dW GEMM.  Only one chunk's dz is live.
+#include "kd_internal.h"
+#include "kdkl.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// --- timing ---------------------------------------------------------------------
+struct Prof {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[kd::KC_COUNT];
+  hipEvent_t pending[kd::KC_COUNT] = {};
+};
+Prof g_prof;
+std::mutex g_prof_mu;
+
+const char *const kClassNames[kd::KC_COUNT] = {
+    "validate", "fwd_gemm_lse", "gather", "combine_lse_loss", "bwd_gemm_dz",
+    "scatter",  "dh_gemm",      "dh_reduce", "dw_gemm",      "misc"};
+
+#define HIPCHK(expr)                                                                 \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return fail(KD_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));          \
+  } while (0)
+
+#define LAUNCH(cls, expr)                                                            \
+  do {                                                                               \
+    kd::prof_begin(cls, stream);                                                     \
+    hipError_t e_ = (expr);                                                          \
+    kd::prof_end(cls, stream);                                                       \
+    if (e_ != hipSuccess)                                                            \
+      return fail(KD_E_HIP, "launch %s failed: %s", #expr, hipGetErrorString(e_));   \
+  } while (0)
+
+int check_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_t dtype) {
+  if (dtype != KD_F32 && dtype != KD_BF16) return fail(KD_E_ARG, "dtype %d unknown", dtype);
+  if (N < 0) return fail(KD_E_ARG, "N = %lld < 0", (long long)N);
+  if (d < 1 || V < 1 || K < 1) return fail(KD_E_ARG, "d, V and K must be >= 1");
+  if (chunk < 1) return fail(KD_E_ARG, "chunk = %lld < 1", (long long)chunk);
+  if (K > 65536) return fail(KD_E_UNSUPPORTED, "K = %d above 65536", K);
+  if (d % 8 != 0) return fail(KD_E_UNSUPPORTED, "d = %lld is not a multiple of 8", (long long)d);
+  if (d > (1 << 20) || V > (int64_t)1 << 30)
+    return fail(KD_E_UNSUPPORTED, "d or V too large");
+  const int64_t lim = (int64_t)1 << 62;
+  if (N > 0 && (N > lim / d || N > lim / K)) return fail(KD_E_ARG, "N too large");
+  if (V > lim / d) return fail(KD_E_ARG, "V*d too large");
+  return KD_OK;
+}
+
+}  // namespace
+
+namespace kd {
+
+void prof_begin(int cls, hipStream_t s) {
+  if (!g_prof.on) return;
+  hipEvent_t a;
+  if (hipEventCreate(&a) != hipSuccess) return;
+  (void)hipEventRecord(a, s);
+  g_prof.pending[cls] = a;
+}
+
+void prof_end(int cls, hipStream_t s) {
+  if (!g_prof.on || !g_prof.pending[cls]) return;
+  hipEvent_t b;
+  if (hipEventCreate(&b) != hipSuccess) return;
+  (void)hipEventRecord(b, s);
+  g_prof.ev[cls].emplace_back(g_prof.pending[cls], b);
+  g_prof.pending[cls] = nullptr;
+}
+
+bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
+                 Layout *L) {
+  const int64_t es = dtype == KD_BF16 ? 2 : 4;
+  const int64_t Nn = N > 0 ? N : 1;
+  L->C = chunk < Nn ? chunk : Nn;
+  L->C_alloc = rup(L->C, kTile);
+  L->V_pad = rup(V, kTile);
+  L->d_pad = rup(d, kTile);
+  L->n_lse = (V + kLseRows - 1) / kLseRows;
+  // Split the vocabulary of the dh GEMM so that about three workgroups per CU run.
+  const int64_t tiles = (L->d_pad / kTile) * (L->C_alloc / kTile);
+  const int64_t kstep = dtype == KD_BF16 ? 64 : 32;
+  int64_t ns = (768 + tiles - 1) / tiles;
+  const int64_t max_by_k = L->V_pad / (8 * kstep);  // at least 8 k-steps per split
+  if (ns > max_by_k) ns = max_by_k;
+  if (ns > 16) ns = 16;
+  if (ns < 1) ns = 1;
+  L->k_split = rup((L->V_pad + ns - 1) / ns, kstep);
+  L->nsplit = (int)((L->V_pad + L->k_split - 1) / L->k_split);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (size_t)rup((int64_t)bytes, 256);
+    return o;
+  };
+  L->off_flags = take(64);
+  L->off_acc = take(64);
+  L->off_partials = take((size_t)L->n_lse * L->C_alloc * sizeof(float2));
+  L->off_lse = take((size_t)L->C_alloc * 4);
+  L->off_sM = take((size_t)L->C_alloc * 4);
+  L->off_s = take((size_t)L->C_alloc * 4);
+  L->off_rowterm = take((size_t)L->C_alloc * 8);
+  L->off_zg = take((size_t)L->C_alloc * K * 4);
+  L->off_dz = take((size_t)L->C_alloc * L->V_pad * es);
+  L->off_dhpart = take((size_t)L->nsplit * L->C_alloc * L->d_pad * 4);
+  L->total = off;
+  return true;
+}
+
+}  // namespace kd
+
+extern "C" {
+
+int kd_version(void) { return 1; }
+
+const char *kd_last_error(void) { return g_err; }
+
+int kd_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_t dtype,
+                       size_t *bytes_out) {
+  g_err[0] = 0;
+  if (!bytes_out) return fail(KD_E_ARG, "bytes_out is NULL");
+  int rc = check_sizes(N, d, V, K, chunk, dtype);
+  if (rc != KD_OK) return rc;
+  kd::Layout L;
+  kd::make_layout(N, d, V, K, chunk, dtype, &L);
+  *bytes_out = L.total;
+  return KD_OK;
+}
+
+int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int32_t *topk_idx,
+                          const float *topk_p, const uint8_t *loss_mask, int64_t N, int64_t d,
+                          int64_t V, int32_t K, int64_t chunk, float *loss, void *dh, float *dW,
+                          float *row_loss, float *row_lse, float *zg, void *workspace,
+                          size_t workspace_bytes, void *stream_v) {
+  g_err[0] = 0;
+  int rc = check_sizes(N, d, V, K, chunk, dtype);
+  if (rc != KD_OK) return rc;
+  if (!W || !loss || !dW || !workspace) return fail(KD_E_ARG, "W, loss, dW and workspace are required");
+  if (N > 0 && (!h || !topk_idx || !topk_p || !dh))
+    return fail(KD_E_ARG, "h, topk_idx, topk_p and dh are required when N > 0");
+  auto mis = [](const void *p, uintptr_t a) { return p && ((uintptr_t)p % a) != 0; };
+  if (mis(h, 16) || mis(W, 16) || mis(dh, 16) || mis(dW, 16))
+    return fail(KD_E_ARG, "h, W, dh and dW must be 16-byte aligned");
+  if (mis(topk_idx, 4) || mis(topk_p, 4) || mis(loss, 4) || mis(row_loss, 4) ||
+      mis(row_lse, 4) || mis(zg, 4))
+    return fail(KD_E_ARG, "index, probability and float outputs must be 4-byte aligned");
+  if (mis(workspace, 256)) return fail(KD_E_ARG, "workspace must be 256-byte aligned");
+  kd::Layout L;
+  kd::make_layout(N, d, V, K, chunk, dtype, &L);
+  if (workspace_bytes < L.total)
+    return fail(KD_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+
+  hipStream_t stream = (hipStream_t)stream_v;
+  char *ws = (char *)workspace;
+  int *flags = (int *)(ws + L.off_flags);
+  unsigned long long *dcount = (unsigned long long *)(ws + L.off_flags + 8);
+  double *acc = (double *)(ws + L.off_acc);
+  float2 *partials = (float2 *)(ws + L.off_partials);
+  float *lse = (float *)(ws + L.off_lse);
+  float *sM = (float *)(ws + L.off_sM);
+  float *srow = (float *)(ws + L.off_s);
+  double *rowterm = (double *)(ws + L.off_rowterm);
+  float *zg_ws = (float *)(ws + L.off_zg);
+  void *dz = ws + L.off_dz;
+  float *dhpart = (float *)(ws + L.off_dhpart);
+  const int64_t es = dtype == KD_BF16 ? 2 : 4;
+
+  if (N == 0) {
+    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
+    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dW, (size_t)V * d * 4, stream));
+    return KD_OK;
+  }
+
+  // Validate the teacher entries and count the mask; the only host synchronisation.
+  LAUNCH(kd::KC_MISC, kd::launch_fill_zero(ws + L.off_flags, L.off_acc - L.off_flags + 64, stream));
+  LAUNCH(kd::KC_VALIDATE,
+         kd::launch_validate(topk_idx, topk_p, N * (int64_t)K, V, loss_mask, N, flags, dcount, stream));
+  struct {
+    int flags[2];
+    unsigned long long count;
+  } hostv;
+  HIPCHK(hipMemcpyAsync(&hostv, flags, sizeof hostv, hipMemcpyDeviceToHost, stream));
+  HIPCHK(hipStreamSynchronize(stream));
+  if (hostv.flags[0])
+    return fail(KD_E_INDEX, "a teacher index is outside [0, %lld) or a probability is negative or not finite",
+                (long long)V);
+  const int64_t count = loss_mask ? (int64_t)hostv.count : N;
+  const bool want_rows = row_loss || row_lse || zg;
+
+  if (count == 0) {
+    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
+    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dW, (size_t)V * d * 4, stream));
+    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dh, (size_t)N * d * es, stream));
+    if (!want_rows) return KD_OK;
+  }
+  const float inv_count = count > 0 ? (float)(1.0 / (double)count) : 0.f;
+
+  int chunk_i = 0;
+  for (int64_t c0 = 0; c0 < N; c0 += L.C, ++chunk_i) {
+    const int64_t rows = (N - c0) < L.C ? (N - c0) : L.C;
+    const char *h_c = (const char *)h + c0 * d * es;
+    const int32_t *idx_c = topk_idx + c0 * K;
+    const float *p_c = topk_p + c0 * K;
+    const uint8_t *mask_c = loss_mask ? loss_mask + c0 : nullptr;
+    float *zg_c = zg ? zg + c0 * K : zg_ws;
+
+    LAUNCH(kd::KC_FWD_GEMM,
+           kd::launch_fwd_gemm(dtype, W, h_c, rows, d, V, partials, L.C_alloc, stream));
+    LAUNCH(kd::KC_GATHER, kd::launch_gather(dtype, h_c, W, idx_c, rows, d, K, zg_c, stream));
+    LAUNCH(kd::KC_COMBINE,
+           kd::launch_combine(partials, L.n_lse, L.C_alloc, zg_c, p_c, mask_c, rows, K, inv_count,
+                              lse, sM, srow, rowterm, row_loss ? row_loss + c0 : nullptr,
+                              row_lse ? row_lse + c0 : nullptr, stream));
+    if (count == 0) continue;  // forward-only sweep for the per-row outputs
+    LAUNCH(kd::KC_MISC, kd::launch_accum_loss(rowterm, rows, acc, stream));
+    LAUNCH(kd::KC_BWD_GEMM,
+           kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse, sM, dz, L.V_pad, stream));
+    LAUNCH(kd::KC_SCATTER,
+           kd::launch_scatter(dtype, dz, L.V_pad, idx_c, p_c, srow, rows, K, stream));
+    LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, rows, d, V, L.V_pad, L.nsplit,
+                                              L.k_split, dhpart, L.d_pad, L.C_alloc, stream));
+    LAUNCH(kd::KC_DH_REDUCE, kd::launch_dh_reduce(dtype, dhpart, L.nsplit, L.C_alloc, L.d_pad,
+                                                  rows, d, (char *)dh + c0 * d * es, stream));
+    LAUNCH(kd::KC_DW_GEMM,
+           kd::launch_dw_gemm(dtype, dz, h_c, rows, d, V, L.V_pad, dW, chunk_i > 0, stream));
+  }
+  if (count > 0) LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));
+  return KD_OK;
+}
+
+int kd_profile_enable(int on) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof.on = on != 0;
+  return KD_OK;
+}
+
+int kd_profile_num_classes(void) { return kd::KC_COUNT; }
+
+const char *kd_profile_class_name(int cls) {
+  return (cls >= 0 && cls < kd::KC_COUNT) ? kClassNames[cls] : "";
+}
+
+int kd_profile_read(int cls, double *total_ms, int64_t *launches) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  if (cls < 0 || cls >= kd::KC_COUNT || !total_ms || !launches)
+    return fail(KD_E_ARG, "bad profile class or null output");
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto &pr : g_prof.ev[cls]) {
+    float ms = 0.f;
+    if (hipEventSynchronize(pr.second) == hipSuccess &&
+        hipEventElapsedTime(&ms, pr.first, pr.second) == hipSuccess) {
+      tot += ms;
+      ++n;
+    }
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  g_prof.ev[cls].clear();
+  *total_ms = tot;
+  *launches = n;
+  return KD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Internal interface between the C-ABI front end (kd_api.hip) and the gfx950
+// kernels (kd_kernels.hip).  Not installed; not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace kd {
+
+// Output tile of every GEMM launch: 256 x 256, four waves of 128 x 128.
+constexpr int kTile = 256;
+// Vocabulary rows per (max, sum-exp) partial written by the forward GEMM (one wave's rows).
+constexpr int kLseRows = 128;
+
+// Kernel classes for timing (kd_profile_*).
+enum KClass {
+  KC_VALIDATE = 0,
+  KC_FWD_GEMM,     // logits GEMM + per-tile max / sum-exp
+  KC_GATHER,       // logits at the teacher's indices
+  KC_COMBINE,      // logsumexp + per-token loss
+  KC_BWD_GEMM,     // logits recomputed + dense dz
+  KC_SCATTER,      // sparse teacher correction of dz
+  KC_DH_GEMM,      // dh partials (split over the vocabulary)
+  KC_DH_REDUCE,    // dh partials summed and rounded
+  KC_DW_GEMM,      // dW accumulation
+  KC_MISC,         // fills, loss accumulation and finalisation
+  KC_COUNT
+};
+
+// Workspace carve-up; every offset is a multiple of 256 bytes.
+struct Layout {
+  int64_t C;          // token rows per chunk (min(chunk, N))
+  int64_t C_alloc;    // C rounded up to the tile
+  int64_t V_pad;      // V rounded up to the tile (row pitch of dz)
+  int64_t d_pad;      // d rounded up to the tile (row pitch of the dh partials)
+  int64_t n_lse;      // ceil(V / kLseRows)
+  int nsplit;         // vocabulary splits of the dh GEMM
+  int64_t k_split;    // vocabulary rows per split (multiple of the k-step)
+  size_t off_flags, off_acc, off_partials, off_lse, off_sM, off_s, off_rowterm, off_zg,
+      off_dz, off_dhpart, total;
+};
+
+bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
+                 Layout *L);
+
+// --- launchers (all asynchronous on `s`; return hipSuccess or the launch error) ---
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_validate(const int32_t *idx, const float *p, int64_t NK, int64_t V,
+                           const uint8_t *mask, int64_t N, int *flags,
+                           unsigned long long *count, hipStream_t s);
+hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows,
+                           int64_t d, int64_t V, float2 *partials, int64_t ld_part,
+                           hipStream_t s);
+hipError_t launch_gather(int dtype, const void *h_c, const void *W, const int32_t *idx_c,
+                         int64_t rows, int64_t d, int32_t K, float *zg, hipStream_t s);
+hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part,
+                          const float *zg, const float *p_c, const uint8_t *mask_c,
+                          int64_t rows, int32_t K, float inv_count, float *lse, float *sM,
+                          float *srow, double *rowterm, float *row_loss, float *row_lse,
+                          hipStream_t s);
+hipError_t launch_accum_loss(const double *rowterm, int64_t rows, double *acc, hipStream_t s);
+hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s);
+hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
+                           int64_t V, const float *lse, const float *sM, void *dz,
+                           int64_t V_pad, hipStream_t s);
+hipError_t launch_scatter(int dtype, void *dz, int64_t V_pad, const int32_t *idx_c,
+                          const float *p_c, const float *srow, int64_t rows, int32_t K,
+                          hipStream_t s);
+hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, int64_t rows, int64_t d,
+                          int64_t V, int64_t V_pad, int nsplit, int64_t k_split,
+                          float *part, int64_t d_pad, int64_t C_alloc, hipStream_t s);
+hipError_t launch_dh_reduce(int dtype, const float *part, int nsplit, int64_t C_alloc,
+                            int64_t d_pad, int64_t rows, int64_t d, void *dh, hipStream_t s);
+hipError_t launch_dw_gemm(int dtype, const void *dz, const void *h_c, int64_t rows, int64_t d,
+                          int64_t V, int64_t V_pad, float *dW, int accumulate,
+                          hipStream_t s);
+
+// --- timing hooks (kd_api.hip) ---
+void prof_begin(int cls, hipStream_t s);
+void prof_end(int cls, hipStream_t s);
+
+}  // namespace kd

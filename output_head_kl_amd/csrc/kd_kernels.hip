@@ -1,0 +1,789 @@
+// gfx950 kernels of the fused, chunked top-K KL loss.
+//
+// Per token chunk (see kd_api.hip for the sequence):
+//   forward GEMM   z^T tile = W_tile . h_tile^T on MFMA, epilogue: per-token max and
+//                  sum of exp over the tile's vocabulary rows (no logits stored);
+//   gather         z at the teacher's K indices;
+//   combine        logsumexp over the tiles, per-token loss;
+//   backward GEMM  z recomputed, epilogue: dz = (mask/count) * M * exp(z - lse), bf16;
+//   scatter        dz -= (mask/count) * p at the teacher's indices;
+//   dh GEMM        dh = dz . W (split over the vocabulary, fp32 partials, then reduced);
+//   dW GEMM        dW += dz^T . h (fp32 read-modify-write).
+// "Recompute backward: repeat projection work during backpropagation to save memory"
+// (thorstenmeyerai.com infographic); only one chunk's dz is ever live.
+#include "kd_internal.h"
+
+#include <cstdint>
+
+namespace kd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) {
+  return __uint_as_float(((unsigned int)b) << 16);
+}
+// Round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  unsigned int u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
+  return (unsigned int)f32_to_bf16(lo) | ((unsigned int)f32_to_bf16(hi) << 16);
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lanes l and l^32 hold the two halves of a token's values; combine them.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (bid % 8).  Give each XCD a
+// contiguous range of tile ids so that tiles sharing operands share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int T) {
+  const int q = T >> 3, r = T & 7, x = bid & 7, j = bid >> 3;
+  return x * q + (x < r ? x : r) + j;
+}
+
+// ---------------------------------------------------------------------------------
+// MFMA GEMM core
+//
+// D[m][n] = sum_k A[m][k] * B[k][n] over one 256 x 256 tile, K in steps of one
+// 128-byte row chunk per operand row (64 bf16 or 32 fp32).  An operand is either
+//   KC: stored [mn][k] (k contiguous) -> LDS [256 rows][128 B], 16-B chunks XOR
+//       swizzled by row, fragments read with ds_read_b128;
+//   MC: stored [k][mn] (mn contiguous) -> LDS [k rows][256 mn] padded rows,
+//       fragments read transposed (ds_read_b64_tr_b16 for bf16).
+// Each wave owns 128 x 128 of the tile as 4 x 4 blocks of the 32x32 MFMA;
+// accumulator element i of lane l in block (rb, cb) is row
+// rb*32 + (i/4)*8 + (l/32)*4 + i%4 and column cb*32 + l%32 of the wave's square.
+// ---------------------------------------------------------------------------------
+enum { OP_KC = 0, OP_MC = 1 };
+
+struct Operand {
+  const void *ptr;  // element (mn, k) at KC: ptr[mn*ld + k], MC: ptr[k*ld + mn]
+  long long ld;     // elements
+  int mn_ext;       // rows/cols with mn >= mn_ext read as zero
+  int k_ext;        // k >= k_ext read as zero
+};
+
+struct GemmGrid {
+  int ntm, ntn, nsplit;
+  int k_len;    // k range of one split (multiple of the k-step)
+  int k_total;  // loop bound
+  int order;    // 0: n-tile index fastest, 1: m-tile index fastest
+};
+
+template <int DT> struct Elem;
+template <> struct Elem<1> {  // bf16
+  static constexpr int CH = 8, BK = 64, ES = 2, MC_PITCH = 576, MC_ROWS = 64;
+};
+template <> struct Elem<0> {  // fp32
+  static constexpr int CH = 4, BK = 32, ES = 4, MC_PITCH = 1088, MC_ROWS = 32;
+};
+
+template <int DT, int KIND> struct OpLds {
+  static constexpr int BYTES = KIND == OP_KC ? 256 * 128 : Elem<DT>::MC_ROWS * Elem<DT>::MC_PITCH;
+};
+
+template <int DT, int KIND>
+__device__ __forceinline__ void load_stage(u32x4 (&r)[8], const Operand &op, int mn0, int k0,
+                                           int t) {
+  constexpr int CH = Elem<DT>::CH, ES = Elem<DT>::ES;
+  const char *base = (const char *)op.ptr;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = t + 256 * i;
+    int mn, k;
+    if (KIND == OP_KC) {
+      mn = mn0 + (q >> 3);
+      k = k0 + (q & 7) * CH;
+    } else if (DT == 1) {
+      k = k0 + (q >> 5);
+      mn = mn0 + (q & 31) * CH;
+    } else {
+      k = k0 + (q >> 6);
+      mn = mn0 + (q & 63) * CH;
+    }
+    const bool ok = mn < op.mn_ext && k < op.k_ext;
+    const long long e = KIND == OP_KC ? (long long)mn * op.ld + k : (long long)k * op.ld + mn;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ok) v = *(const u32x4 *)(base + e * ES);
+    r[i] = v;
+  }
+}
+
+template <int DT, int KIND>
+__device__ __forceinline__ void store_stage(char *lds, const u32x4 (&r)[8], int t) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = t + 256 * i;
+    int off;
+    if (KIND == OP_KC) {
+      const int row = q >> 3, kc = q & 7;
+      off = row * 128 + ((kc ^ (row & 7)) << 4);
+    } else if (DT == 1) {
+      off = (q >> 5) * Elem<1>::MC_PITCH + (q & 31) * 16;
+    } else {
+      off = (q >> 6) * Elem<0>::MC_PITCH + (q & 63) * 16;
+    }
+    *(LDS_AS u32x4 *)((LDS_AS char *)lds + off) = r[i];
+  }
+}
+
+// Fragment of 32 rows r0..r0+31 for k-substep ks (16 bf16 or 8 fp32 of k).
+template <int DT, int KIND> struct Frag;
+
+template <> struct Frag<1, OP_KC> {
+  typedef bf16x8 type;
+  static __device__ __forceinline__ type load(const char *lds, int r0, int ks, int lane) {
+    const int row = r0 + (lane & 31), kc = ks * 2 + (lane >> 5);
+    return *(const LDS_AS bf16x8 *)((const LDS_AS char *)lds + row * 128 + ((kc ^ (row & 7)) << 4));
+  }
+};
+template <> struct Frag<1, OP_MC> {
+  typedef bf16x8 type;
+  // ds_read_b64_tr_b16: in each 16-lane group, lane j receives element j%4 of the
+  // 8 bytes loaded by lanes j/4 + 4r, r = 0..3.  Lane s of the group loads the 4
+  // values at [k = kb + s/4][m = mb + 4*(s%4) ..], so lane j gets [kb..kb+3][mb + j].
+  static __device__ __forceinline__ type load(const char *lds, int r0, int ks, int lane) {
+    const int s = lane & 15, g = lane >> 4;
+    const int m = r0 + (g & 1) * 16 + 4 * (s & 3);
+    const int k = ks * 16 + (g >> 1) * 8 + (s >> 2);
+    const LDS_AS char *b = (const LDS_AS char *)lds;
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_AS s16x4 *)(b + k * Elem<1>::MC_PITCH + m * 2));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_AS s16x4 *)(b + (k + 4) * Elem<1>::MC_PITCH + m * 2));
+    s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+template <> struct Frag<0, OP_KC> {
+  typedef f32x4 type;
+  static __device__ __forceinline__ type load(const char *lds, int r0, int ks, int lane) {
+    const int row = r0 + (lane & 31), kc = ks * 2 + (lane >> 5);
+    return *(const LDS_AS f32x4 *)((const LDS_AS char *)lds + row * 128 + ((kc ^ (row & 7)) << 4));
+  }
+};
+template <> struct Frag<0, OP_MC> {
+  typedef f32x4 type;
+  static __device__ __forceinline__ type load(const char *lds, int r0, int ks, int lane) {
+    const int m = r0 + (lane & 31), k = ks * 8 + (lane >> 5) * 4;
+    const LDS_AS char *b = (const LDS_AS char *)lds;
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = *(const LDS_AS float *)(b + (k + e) * Elem<0>::MC_PITCH + m * 4);
+    return v;
+  }
+};
+
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// fp32: the 16-byte fragment holds 4 k values per lane; k-slot l/32 of MFMA e uses
+// element e, so four 32x32x2 MFMAs cover the same 8 k as one bf16 fragment pair.
+__device__ __forceinline__ f32x16 mma(f32x4 a, f32x4 b, f32x16 c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], b[3], c, 0, 0, 0);
+  return c;
+}
+
+template <int DT, int AK, int BKIND, class Epi>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
+  constexpr int A_BYTES = OpLds<DT, AK>::BYTES, B_BYTES = OpLds<DT, BKIND>::BYTES;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int BK = Elem<DT>::BK;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int T = gridDim.x;
+  const int lin = xcd_remap(blockIdx.x, T);
+  const int per_split = G.ntm * G.ntn;
+  const int split = lin / per_split;
+  const int rem = lin - split * per_split;
+  int tm, tn;
+  if (G.order == 0) {
+    tm = rem / G.ntn;
+    tn = rem - tm * G.ntn;
+  } else {
+    tn = rem / G.ntm;
+    tm = rem - tn * G.ntm;
+  }
+  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int kb = split * G.k_len;
+  const int ke = min(G.k_total, kb + G.k_len);
+  const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wr = w >> 1, wc = w & 1;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  u32x4 ra[8], rbuf[8];
+  if (nk > 0) {
+    load_stage<DT, AK>(ra, A, m0, kb, t);
+    load_stage<DT, BKIND>(rbuf, B, n0, kb, t);
+    store_stage<DT, AK>(smem, ra, t);
+    store_stage<DT, BKIND>(smem + A_BYTES, rbuf, t);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < nk; ++it) {
+    const int cur = it & 1;
+    const bool more = it + 1 < nk;
+    if (more) {
+      load_stage<DT, AK>(ra, A, m0, kb + (it + 1) * BK, t);
+      load_stage<DT, BKIND>(rbuf, B, n0, kb + (it + 1) * BK, t);
+    }
+    const char *la = smem + cur * STAGE;
+    const char *lb = la + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      typename Frag<DT, AK>::type fa[4];
+      typename Frag<DT, BKIND>::type fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = Frag<DT, AK>::load(la, wr * 128 + i * 32, ks, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = Frag<DT, BKIND>::load(lb, wc * 128 + j * 32, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma(fa[i], fb[j], acc[i][j]);
+    }
+    if (more) {
+      char *nxt = smem + (cur ^ 1) * STAGE;
+      store_stage<DT, AK>(nxt, ra, t);
+      store_stage<DT, BKIND>(nxt + A_BYTES, rbuf, t);
+    }
+    __syncthreads();
+  }
+  epi(acc, m0 + wr * 128, n0 + wc * 128, lane, split);
+}
+
+// ---------------------------------------------------------------------------------
+// Epilogues
+// ---------------------------------------------------------------------------------
+// Forward: tile rows are vocabulary entries v, columns are tokens c.  Each lane holds
+// 64 of a token's 128 values in the wave's square; lane l^32 holds the rest.
+struct EpiFwdLse {
+  float2 *part;   // [n_lse][ld] (max, sum exp(z - max)) per 128 vocabulary rows
+  long long ld;
+  int V, rows;
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
+                                             int) const {
+    if (m0 >= V) return;
+    const bool full = m0 + 128 <= V;
+    const int vl = m0 + (lane >> 5) * 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
+          if (full || v < V) mx = fmaxf(mx, acc[rb][cb][i]);
+        }
+      mx = halves_max(mx);
+      const float mx2 = mx * kLog2e;
+      float s = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
+          if (full || v < V) s += fast_exp2(fmaf(acc[rb][cb][i], kLog2e, -mx2));
+        }
+      s = halves_sum(s);
+      const int c = n0 + cb * 32 + (lane & 31);
+      if (lane < 32 && c < rows) part[(long long)(m0 / kLseRows) * ld + c] = make_float2(mx, s);
+    }
+  }
+};
+
+// Backward: dz[c][v] = sM[c] * exp(z - lse[c]) for v < V, 0 for V <= v < V_pad.
+template <int DT>
+struct EpiBwdDz {
+  void *dz;
+  long long ld;  // V_pad
+  const float *lse, *sM;
+  int V, rows;
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
+                                             int) const {
+    const int vl = m0 + (lane >> 5) * 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int c = n0 + cb * 32 + (lane & 31);
+      if (c >= rows) continue;
+      const float l2 = lse[c] * kLog2e;
+      const float a = sM[c];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int v0 = vl + rb * 32 + g * 8;
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[e] = (v0 + e < V) ? a * fast_exp2(fmaf(acc[rb][cb][g * 4 + e], kLog2e, -l2)) : 0.f;
+          if (DT == 1) {
+            u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+            *(u32x2 *)((unsigned short *)dz + (long long)c * ld + v0) = pk;
+          } else {
+            *(f32x4 *)((float *)dz + (long long)c * ld + v0) = f32x4{x[0], x[1], x[2], x[3]};
+          }
+        }
+    }
+  }
+};
+
+// dh split: tile rows are hidden units j, columns tokens c; fp32 partial per split.
+struct EpiDhPart {
+  float *part;
+  long long split_stride, ld;  // C_alloc*d_pad, d_pad
+  int rows;
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
+                                             int split) const {
+    float *base = part + split * split_stride;
+    const int jl = m0 + (lane >> 5) * 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int c = n0 + cb * 32 + (lane & 31);
+      if (c >= rows) continue;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j = jl + rb * 32 + g * 8;
+          const f32x4 v = {acc[rb][cb][g * 4], acc[rb][cb][g * 4 + 1], acc[rb][cb][g * 4 + 2],
+                           acc[rb][cb][g * 4 + 3]};
+          *(f32x4 *)(base + (long long)c * ld + j) = v;
+        }
+    }
+  }
+};
+
+// dW: tile rows are hidden units j, columns vocabulary entries v.
+struct EpiDw {
+  float *dW;
+  int d, V, accumulate;
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
+                                             int) const {
+    const int jl = m0 + (lane >> 5) * 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int v = n0 + cb * 32 + (lane & 31);
+      if (v >= V) continue;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j = jl + rb * 32 + g * 8;
+          if (j >= d) continue;
+          f32x4 x = {acc[rb][cb][g * 4], acc[rb][cb][g * 4 + 1], acc[rb][cb][g * 4 + 2],
+                     acc[rb][cb][g * 4 + 3]};
+          f32x4 *p = (f32x4 *)(dW + (long long)v * d + j);
+          if (accumulate) x += *p;
+          *p = x;
+        }
+    }
+  }
+};
+
+template <int DT, int AK, int BKIND, class Epi>
+static hipError_t run_gemm(const Operand &A, const Operand &B, const GemmGrid &G, const Epi &epi,
+                           hipStream_t s) {
+  const long long T = (long long)G.ntm * G.ntn * G.nsplit;
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_kernel<DT, AK, BKIND, Epi>), dim3((unsigned)T), dim3(256), 0, s, A,
+                     B, G, epi);
+  return hipGetLastError();
+}
+
+static inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// ---------------------------------------------------------------------------------
+// GEMM launchers
+// ---------------------------------------------------------------------------------
+hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
+                           int64_t V, float2 *partials, int64_t ld_part, hipStream_t s) {
+  Operand A{W, d, (int)V, (int)d};
+  Operand B{h_c, d, (int)rows, (int)d};
+  GemmGrid G{cdiv(V, kTile), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
+  EpiFwdLse e{partials, ld_part, (int)V, (int)rows};
+  return dtype == 1 ? run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s)
+                    : run_gemm<0, OP_KC, OP_KC>(A, B, G, e, s);
+}
+
+hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
+                           int64_t V, const float *lse, const float *sM, void *dz,
+                           int64_t V_pad, hipStream_t s) {
+  Operand A{W, d, (int)V, (int)d};
+  Operand B{h_c, d, (int)rows, (int)d};
+  GemmGrid G{cdiv(V, kTile), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
+  if (dtype == 1) {
+    EpiBwdDz<1> e{dz, V_pad, lse, sM, (int)V, (int)rows};
+    return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
+  }
+  EpiBwdDz<0> e{dz, V_pad, lse, sM, (int)V, (int)rows};
+  return run_gemm<0, OP_KC, OP_KC>(A, B, G, e, s);
+}
+
+hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, int64_t rows, int64_t d,
+                          int64_t V, int64_t V_pad, int nsplit, int64_t k_split, float *part,
+                          int64_t d_pad, int64_t C_alloc, hipStream_t s) {
+  // D[j][c] = sum_v W[v][j] dz[c][v]: A = W as MC ([v][j]), B = dz as KC ([c][v]).
+  Operand A{W, d, (int)d, (int)V};
+  Operand B{dz, V_pad, (int)rows, (int)V_pad};
+  GemmGrid G{cdiv(d, kTile), cdiv(rows, kTile), nsplit, (int)k_split, (int)V_pad, 0};
+  EpiDhPart e{part, C_alloc * d_pad, d_pad, (int)rows};
+  return dtype == 1 ? run_gemm<1, OP_MC, OP_KC>(A, B, G, e, s)
+                    : run_gemm<0, OP_MC, OP_KC>(A, B, G, e, s);
+}
+
+hipError_t launch_dw_gemm(int dtype, const void *dz, const void *h_c, int64_t rows, int64_t d,
+                          int64_t V, int64_t V_pad, float *dW, int accumulate, hipStream_t s) {
+  // D[j][v] = sum_c h[c][j] dz[c][v]: A = h as MC ([c][j]), B = dz as MC ([c][v]).
+  Operand A{h_c, d, (int)d, (int)rows};
+  Operand B{dz, V_pad, (int)V_pad, (int)rows};
+  GemmGrid G{cdiv(d, kTile), cdiv(V, kTile), 1, (int)rows, (int)rows, 1};
+  EpiDw e{dW, (int)d, (int)V, accumulate};
+  return dtype == 1 ? run_gemm<1, OP_MC, OP_MC>(A, B, G, e, s)
+                    : run_gemm<0, OP_MC, OP_MC>(A, B, G, e, s);
+}
+
+// ---------------------------------------------------------------------------------
+// Small kernels
+// ---------------------------------------------------------------------------------
+__global__ void k_fill_zero(unsigned int *p, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
+  const long long n = (long long)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
+  hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, s, (unsigned int *)p, n);
+  return hipGetLastError();
+}
+
+// flags[0] |= 1 for an index outside [0, V) or a probability that is negative or not
+// finite; count += number of nonzero mask bytes.
+__global__ void k_validate(const int32_t *idx, const float *p, long long NK, int V,
+                           const uint8_t *mask, long long N, int *flags,
+                           unsigned long long *count) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  const long long g = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  int bad = 0;
+  for (long long i = g; i < NK; i += stride) {
+    const int v = idx[i];
+    const float q = p[i];
+    if (v < 0 || v >= V || !(q >= 0.f) || q == INFINITY) bad = 1;
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flags, 1);
+  unsigned long long c = 0;
+  if (mask)
+    for (long long i = g; i < N; i += stride) c += mask[i] != 0;
+  __shared__ unsigned long long sh[4];
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned long long tot = sh[0] + sh[1] + sh[2] + sh[3];
+    if (tot) atomicAdd(count, tot);
+  }
+}
+
+hipError_t launch_validate(const int32_t *idx, const float *p, int64_t NK, int64_t V,
+                           const uint8_t *mask, int64_t N, int *flags,
+                           unsigned long long *count, hipStream_t s) {
+  long long work = NK > N ? NK : N;
+  int blocks = (int)((work + 255) / 256);
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_validate, dim3(blocks), dim3(256), 0, s, idx, p, (long long)NK, (int)V,
+                     mask, (long long)N, flags, count);
+  return hipGetLastError();
+}
+
+// One wave per token row; four teacher entries at a time.
+template <int DT>
+__global__ void k_gather(const void *h, const void *W, const int32_t *idx, int rows, int d,
+                         int K, float *zg) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  constexpr int CH = DT == 1 ? 8 : 4;
+  const int nchunks = d / CH;
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    long long vrow[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vrow[u] = (k0 + u < K) ? idx[(long long)r * K + k0 + u] : -1;
+    for (int ci = lane; ci < nchunks; ci += 64) {
+      if (DT == 1) {
+        const u32x4 hv = *(const u32x4 *)((const unsigned short *)h + (long long)r * d + ci * CH);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (vrow[u] < 0) continue;
+          const u32x4 wv = *(const u32x4 *)((const unsigned short *)W + vrow[u] * d + ci * CH);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[u] = fmaf(__uint_as_float(hv[e] << 16), __uint_as_float(wv[e] << 16), acc[u]);
+            acc[u] = fmaf(__uint_as_float(hv[e] & 0xFFFF0000u), __uint_as_float(wv[e] & 0xFFFF0000u),
+                          acc[u]);
+          }
+        }
+      } else {
+        const f32x4 hv = *(const f32x4 *)((const float *)h + (long long)r * d + ci * CH);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (vrow[u] < 0) continue;
+          const f32x4 wv = *(const f32x4 *)((const float *)W + vrow[u] * d + ci * CH);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[u] = fmaf(hv[e], wv[e], acc[u]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float sum = wave_sum(acc[u]);
+      if (lane == 0 && k0 + u < K) zg[(long long)r * K + k0 + u] = sum;
+    }
+  }
+}
+
+hipError_t launch_gather(int dtype, const void *h_c, const void *W, const int32_t *idx_c,
+                         int64_t rows, int64_t d, int32_t K, float *zg, hipStream_t s) {
+  const int blocks = cdiv(rows, 4);
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_gather<1>, dim3(blocks), dim3(256), 0, s, h_c, W, idx_c, (int)rows,
+                       (int)d, (int)K, zg);
+  else
+    hipLaunchKernelGGL(k_gather<0>, dim3(blocks), dim3(256), 0, s, h_c, W, idx_c, (int)rows,
+                       (int)d, (int)K, zg);
+  return hipGetLastError();
+}
+
+// 64 token rows per block; wave w folds partials t = w, w+4, ...; lane = row.
+__global__ void k_combine(const float2 *part, int n_lse, long long ld, const float *zg,
+                          const float *p, const uint8_t *mask, int rows, int K, float inv_count,
+                          float *lse_out, float *sM_out, float *s_out, double *rowterm,
+                          float *row_loss, float *row_lse) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = blockIdx.x * 64 + lane;
+  const bool live = r < rows;
+  float m = -INFINITY, sum = 0.f;
+  if (live) {
+    for (int t0 = w; t0 < n_lse; t0 += 16) {
+      float2 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + 4 * u;
+        q[u] = t < n_lse ? part[(long long)t * ld + r] : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (q[u].y == 0.f) continue;
+        if (q[u].x > m) {
+          sum = sum * fast_exp2((m - q[u].x) * kLog2e) + q[u].y;
+          m = q[u].x;
+        } else {
+          sum += q[u].y * fast_exp2((q[u].x - m) * kLog2e);
+        }
+      }
+    }
+  }
+  __shared__ float sm[4][64], ss[4][64];
+  __shared__ double sd[3][4][64];
+  sm[w][lane] = m;
+  ss[w][lane] = sum;
+  // teacher terms: wave w takes k = w, w+4, ...
+  double H = 0.0, PZ = 0.0, Ms = 0.0;
+  if (live) {
+    for (int k = w; k < K; k += 4) {
+      const double q = p[(long long)r * K + k];
+      Ms += q;
+      PZ += q * (double)zg[(long long)r * K + k];
+      if (q > 0.0) H += q * log(q);
+    }
+  }
+  sd[0][w][lane] = H;
+  sd[1][w][lane] = PZ;
+  sd[2][w][lane] = Ms;
+  __syncthreads();
+  if (w == 0 && live) {
+    float M = sm[0][lane];
+    for (int i = 1; i < 4; ++i) M = fmaxf(M, sm[i][lane]);
+    float S = 0.f;
+    for (int i = 0; i < 4; ++i)
+      if (ss[i][lane] != 0.f) S += ss[i][lane] * fast_exp2((sm[i][lane] - M) * kLog2e);
+    const float lse = M + logf(S);
+    double h = 0.0, pz = 0.0, ms = 0.0;
+    for (int i = 0; i < 4; ++i) {
+      h += sd[0][i][lane];
+      pz += sd[1][i][lane];
+      ms += sd[2][i][lane];
+    }
+    const double ell = h - pz + ms * (double)lse;
+    const bool on = mask ? mask[r] != 0 : true;
+    lse_out[r] = lse;
+    sM_out[r] = on ? (float)(ms * (double)inv_count) : 0.f;
+    s_out[r] = on ? inv_count : 0.f;
+    rowterm[r] = on ? ell : 0.0;
+    if (row_loss) row_loss[r] = on ? (float)ell : 0.f;
+    if (row_lse) row_lse[r] = lse;
+  }
+}
+
+hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part,
+                          const float *zg, const float *p_c, const uint8_t *mask_c,
+                          int64_t rows, int32_t K, float inv_count, float *lse, float *sM,
+                          float *srow, double *rowterm, float *row_loss, float *row_lse,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(k_combine, dim3(cdiv(rows, 64)), dim3(256), 0, s, partials, (int)n_lse,
+                     (long long)ld_part, zg, p_c, mask_c, (int)rows, (int)K, inv_count, lse, sM,
+                     srow, rowterm, row_loss, row_lse);
+  return hipGetLastError();
+}
+
+// acc[0] += sum of rowterm[0..rows) in a fixed order (deterministic).
+__global__ void k_accum_loss(const double *rowterm, int rows, double *acc) {
+  __shared__ double sh[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < rows; i += 256) s += rowterm[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) acc[0] += sh[0];
+}
+
+hipError_t launch_accum_loss(const double *rowterm, int64_t rows, double *acc, hipStream_t s) {
+  hipLaunchKernelGGL(k_accum_loss, dim3(1), dim3(256), 0, s, rowterm, (int)rows, acc);
+  return hipGetLastError();
+}
+
+__global__ void k_finalize(const double *acc, long long count, float *loss) {
+  if (threadIdx.x == 0) loss[0] = count > 0 ? (float)(acc[0] / (double)count) : 0.f;
+}
+
+hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s) {
+  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, s, acc, (long long)count, loss);
+  return hipGetLastError();
+}
+
+// dz[r][idx[r][k]] -= s[r] * (sum of p over the row's entries with that index).
+// The first entry of each distinct index does the update, so no two threads touch
+// the same element.
+template <int DT>
+__global__ void k_scatter(void *dz, long long ld, const int32_t *idx, const float *p,
+                          const float *srow, int rows, int K) {
+  const long long g = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (g >= (long long)rows * K) return;
+  const int r = (int)(g / K), k = (int)(g - (long long)r * K);
+  const float sr = srow[r];
+  if (sr == 0.f) return;
+  const int32_t *ir = idx + (long long)r * K;
+  const float *pr = p + (long long)r * K;
+  const int v = ir[k];
+  for (int j = 0; j < k; ++j)
+    if (ir[j] == v) return;
+  float tot = pr[k];
+  for (int j = k + 1; j < K; ++j)
+    if (ir[j] == v) tot += pr[j];
+  if (DT == 1) {
+    unsigned short *q = (unsigned short *)dz + (long long)r * ld + v;
+    *q = f32_to_bf16(bf16_to_f32(*q) - sr * tot);
+  } else {
+    float *q = (float *)dz + (long long)r * ld + v;
+    *q = *q - sr * tot;
+  }
+}
+
+hipError_t launch_scatter(int dtype, void *dz, int64_t V_pad, const int32_t *idx_c,
+                          const float *p_c, const float *srow, int64_t rows, int32_t K,
+                          hipStream_t s) {
+  const long long n = rows * (long long)K;
+  const int blocks = (int)((n + 255) / 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_scatter<1>, dim3(blocks), dim3(256), 0, s, dz, (long long)V_pad, idx_c,
+                       p_c, srow, (int)rows, (int)K);
+  else
+    hipLaunchKernelGGL(k_scatter<0>, dim3(blocks), dim3(256), 0, s, dz, (long long)V_pad, idx_c,
+                       p_c, srow, (int)rows, (int)K);
+  return hipGetLastError();
+}
+
+// dh[r][j..j+3] = sum over splits of part[s][r][j..j+3], rounded once to the output type.
+template <int DT>
+__global__ void k_dh_reduce(const float *part, int nsplit, long long split_stride, long long ld,
+                            int rows, int d, void *dh) {
+  const long long g = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  const int q = d / 4;
+  if (g >= (long long)rows * q) return;
+  const int r = (int)(g / q), j = (int)(g - (long long)r * q) * 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < nsplit; ++sp) acc += *(const f32x4 *)(part + sp * split_stride + r * ld + j);
+  if (DT == 1) {
+    u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *(u32x2 *)((unsigned short *)dh + (long long)r * d + j) = pk;
+  } else {
+    *(f32x4 *)((float *)dh + (long long)r * d + j) = acc;
+  }
+}
+
+hipError_t launch_dh_reduce(int dtype, const float *part, int nsplit, int64_t C_alloc,
+                            int64_t d_pad, int64_t rows, int64_t d, void *dh, hipStream_t s) {
+  const long long n = rows * (d / 4);
+  const int blocks = (int)((n + 255) / 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_dh_reduce<1>, dim3(blocks), dim3(256), 0, s, part, nsplit,
+                       (long long)(C_alloc * d_pad), (long long)d_pad, (int)rows, (int)d, dh);
+  else
+    hipLaunchKernelGGL(k_dh_reduce<0>, dim3(blocks), dim3(256), 0, s, part, nsplit,
+                       (long long)(C_alloc * d_pad), (long long)d_pad, (int)rows, (int)d, dh);
+  return hipGetLastError();
+}
+
+}  // namespace kd

@@ -1,0 +1,108 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad calls on the
+host before touching a device (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import output_head_kl_amd as kd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdkl.h")
+
+OK, E_ARG, E_INDEX, E_WORKSPACE, E_UNSUPPORTED, E_HIP = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kd.library_path()):
+        pytest.fail("libkdkl.so is not built (run __graft_entry__.build())")
+    return kd._lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"kd_workspace_bytes", "kd_chunked_kl_fwd_bwd", "kd_last_error"} <= set(names)
+    raw = ctypes.CDLL(kd.library_path())
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in kdkl.h but not exported"
+
+
+def test_version_and_profile_classes(lib):
+    assert lib.kd_version() >= 1
+    names = kd.profile_classes()
+    assert "fwd_gemm_lse" in names and "dw_gemm" in names and len(names) == len(set(names))
+
+
+def test_workspace_is_independent_of_N_beyond_one_chunk(lib):
+    a = kd.workspace_bytes(32768, 3072, 128256, 100, 2048)
+    b = kd.workspace_bytes(262144, 3072, 128256, 100, 2048)
+    c = kd.workspace_bytes(4096, 3072, 128256, 100, 2048)
+    assert a == b == c
+    assert a % 256 == 0
+    # dz for one chunk (bf16) dominates; no N x V term
+    assert 2048 * 128256 * 2 < a < 2 * 2048 * 128256 * 2 + 600_000_000
+    small = kd.workspace_bytes(100, 3072, 128256, 100, 2048)
+    assert small < a
+
+
+@pytest.mark.parametrize("args,code", [
+    ((10, 12, 100, 4, 8, 1), E_UNSUPPORTED),     # d not a multiple of 8
+    ((10, 16, 100, 0, 8, 1), E_ARG),             # K = 0
+    ((10, 16, 100, 4, 0, 1), E_ARG),             # chunk = 0
+    ((10, 16, 0, 4, 8, 1), E_ARG),               # V = 0
+    ((-1, 16, 100, 4, 8, 1), E_ARG),             # N < 0
+    ((10, 16, 100, 4, 8, 7), E_ARG),             # unknown dtype
+    ((10, 16, 100, 70000, 8, 1), E_UNSUPPORTED),  # K too large
+])
+def test_workspace_query_rejects_bad_sizes(lib, args, code):
+    out = ctypes.c_size_t(0)
+    assert lib.kd_workspace_bytes(*args, ctypes.byref(out)) == code
+    assert lib.kd_last_error()
+
+
+def _call(lib, **kw):
+    """Call the entry point with fake but aligned device addresses; every case below must
+    be rejected by host checks before any device work."""
+    base = dict(h=0x100000, W=0x200000, dtype=1, idx=0x300000, p=0x400000, mask=None, N=64,
+                d=64, V=1000, K=4, chunk=32, loss=0x500000, dh=0x600000, dW=0x700000,
+                row_loss=None, row_lse=None, zg=None, ws=0x800000, wsb=1 << 40, stream=None)
+    base.update(kw)
+    b = base
+    return lib.kd_chunked_kl_fwd_bwd(b["h"], b["W"], b["dtype"], b["idx"], b["p"], b["mask"],
+                                     b["N"], b["d"], b["V"], b["K"], b["chunk"], b["loss"],
+                                     b["dh"], b["dW"], b["row_loss"], b["row_lse"], b["zg"],
+                                     b["ws"], b["wsb"], b["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), E_ARG),
+    (dict(h=None), E_ARG),
+    (dict(idx=None), E_ARG),
+    (dict(dW=None), E_ARG),
+    (dict(loss=None), E_ARG),
+    (dict(ws=None), E_ARG),
+    (dict(h=0x100008), E_ARG),       # h not 16-byte aligned
+    (dict(dW=0x700004), E_ARG),
+    (dict(ws=0x800010), E_ARG),      # workspace not 256-byte aligned
+    (dict(p=0x400002), E_ARG),
+    (dict(d=60), E_UNSUPPORTED),
+    (dict(chunk=0), E_ARG),
+    (dict(wsb=1000), E_WORKSPACE),
+])
+def test_entry_point_rejects_bad_calls_on_host(lib, kw, code):
+    assert _call(lib, **kw) == code
+    assert lib.kd_last_error()
+
+
+def test_workspace_too_small_reports_needed_size(lib):
+    need = kd.workspace_bytes(64, 64, 1000, 4, 32)
+    assert _call(lib, wsb=need - 1) == E_WORKSPACE
+    assert str(need).encode() in lib.kd_last_error()

@@ -1,0 +1,208 @@
+"""HIP path against the CPU oracle, element by element, on the same seeded inputs.
+
+Small and ragged shapes are compared in full (several tiles, a partial last chunk,
+V and d off the tile grid).  The full-size workloads are compared on 512 sampled token
+rows (per-row loss, logsumexp, gathered logits and dh rows, with the batch's own
+count) plus the whole dW of a 512-row sub-batch run through the same kernels, and the
+mean loss is checked against the per-row losses the GPU returns.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, grad_err, max_abs_rel, rel, rel_fro, run, run_raw, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_full(inp, got, dtype=None):
+    dtype = dtype or inp.cfg.dtype
+    ref = oracle.forward_backward(inp.h64(), inp.W64(), inp.idx, inp.p, inp.mask)
+    tol = TOL[dtype]
+    errs = dict(loss=rel(got["loss"][0], ref["loss"]),
+                dh=grad_err(dtype, got["dh"], ref["dh"]),
+                dW=grad_err(dtype, got["dW"], ref["dW"]),
+                row_lse=max_abs_rel(got["row_lse"], ref["row_lse"]),
+                zg=max_abs_rel(got["zg"], ref["zg"]),
+                row_loss=max_abs_rel(got["row_loss"], ref["row_loss"]))
+    print(inp.cfg.name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert errs["loss"] <= tol["loss"], errs
+    assert errs["dh"] <= tol["grad"], errs
+    assert errs["dW"] <= tol["grad"], errs
+    assert errs["row_lse"] <= tol["loss"], errs
+    assert errs["zg"] <= tol["grad"], errs
+    assert errs["row_loss"] <= 10 * tol["loss"], errs
+    masked = inp.mask == 0
+    if masked.any():
+        assert np.all(got["dh"][masked] == 0.0)
+        assert np.all(got["row_loss"][masked] == 0.0)
+    return ref
+
+
+def test_tiny_fp32_config_in_full(torch_cuda):
+    inp = synth.make(0)
+    _check_full(inp, run(inp, torch_cuda))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_shapes_in_full(torch_cuda, dtype):
+    """V, d and N off the tile grid, a partial last chunk, masked rows and a repeated
+    teacher index (scatter-add)."""
+    inp = synth.make(1, seed=77, N=700, d=264, V=3001, K=7, chunk=300, dtype=dtype)
+    inp.mask[[0, 5, 299, 300, 699]] = 0
+    inp.idx[3, 1] = inp.idx[3, 0]
+    inp.idx[650, 6] = inp.idx[650, 2]
+    _check_full(inp, run(inp, torch_cuda))
+
+
+def test_tiny_chunks_and_single_token(torch_cuda):
+    inp = synth.make(0, seed=5, N=37, d=8, V=300, K=3, chunk=1, dtype="bf16")
+    _check_full(inp, run(inp, torch_cuda))
+    one = synth.make(0, seed=6, N=1, d=16, V=5, K=5, chunk=4, dtype="f32")
+    _check_full(one, run(one, torch_cuda))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gather_probe_is_bit_exact(torch_cuda, dtype):
+    """h_n = (2^16, 2^8, 1, 0, ...), W[j] = (j >> 16, (j >> 8) & 255, j & 255, 0, ...):
+    every value is exact in bf16 and every partial sum is an exact fp32 integer, so
+    z[n, j] = j in any summation order and the gathered logits must equal the indices."""
+    N, d, V, K = 300, 16, 70001, 24
+    inp = synth.make(0, seed=9, N=N, d=d, V=V, K=K, chunk=128, dtype=dtype)
+    h = np.zeros((N, d), np.float32); h[:, 0] = 2.0**16; h[:, 1] = 2.0**8; h[:, 2] = 1.0
+    j = np.arange(V)
+    W = np.zeros((V, d), np.float32)
+    W[:, 0] = j >> 16; W[:, 1] = (j >> 8) & 255; W[:, 2] = j & 255
+    if dtype == "bf16":
+        inp.h, inp.W = synth.f32_to_bf16_bits(h), synth.f32_to_bf16_bits(W)
+    else:
+        inp.h, inp.W = h, W
+    got = run(inp, torch_cuda)
+    assert np.array_equal(got["zg"], inp.idx.astype(np.float64))
+
+
+def test_chunk_invariance_and_determinism(torch_cuda):
+    inp = synth.make(1, seed=11, N=520, d=128, V=5000, K=9, chunk=64)
+    runs = [run(inp, torch_cuda, chunk=c) for c in (64, 128, 1000, 520)]
+    again = run(inp, torch_cuda, chunk=64)
+    for k in ("loss", "dh", "dW", "row_lse", "zg"):
+        assert np.array_equal(runs[0][k], again[k]), f"{k} not bitwise reproducible"
+    for r in runs[1:]:
+        assert rel(r["loss"][0], runs[0]["loss"][0]) < 1e-5
+        assert rel_fro(r["dh"], runs[0]["dh"]) < 1e-2
+        assert rel_fro(r["dW"], runs[0]["dW"]) < 1e-2
+        np.testing.assert_array_equal(r["zg"], runs[0]["zg"])
+
+
+def test_all_masked_and_empty(torch_cuda):
+    inp = synth.make(0, seed=12, N=40, d=32, V=700, K=5, chunk=16)
+    inp.mask[:] = 0
+    got = run(inp, torch_cuda)
+    assert got["loss"][0] == 0.0 and not got["dh"].any() and not got["dW"].any()
+    ref = oracle.forward_backward(inp.h64(), inp.W64(), inp.idx, inp.p, inp.mask)
+    assert max_abs_rel(got["row_lse"], ref["row_lse"]) < 1e-5
+    assert not got["row_loss"].any()
+    empty = synth.make(0, seed=13, N=0, d=32, V=700, K=5, chunk=16)
+    got = run(empty, torch_cuda)
+    assert got["loss"][0] == 0.0 and not got["dW"].any() and got["dh"].shape == (0, 32)
+
+
+@pytest.mark.parametrize("bad", ["idx_high", "idx_negative", "p_negative", "p_nan", "p_inf"])
+def test_invalid_teacher_entry_is_rejected_with_outputs_untouched(torch_cuda, bad):
+    torch = torch_cuda
+    import output_head_kl_amd as kd
+    inp = synth.make(0, seed=14, N=64, d=32, V=500, K=4, chunk=32)
+    if bad == "idx_high":
+        inp.idx[17, 2] = 500
+    elif bad == "idx_negative":
+        inp.idx[63, 0] = -3
+    elif bad == "p_negative":
+        inp.p[1, 1] = -1e-3
+    elif bad == "p_nan":
+        inp.p[40, 3] = np.nan
+    else:
+        inp.p[0, 0] = np.inf
+    h, W, idx, p, mask = to_device(inp, torch)
+    lib = kd._lib()
+    loss = torch.full((1,), 7.0, device="cuda")
+    dh = torch.full((64, 32), 7.0, device="cuda")
+    dW = torch.full((500, 32), 7.0, device="cuda")
+    ws = torch.empty(kd.workspace_bytes(64, 32, 500, 4, 32, kd.KD_F32), dtype=torch.uint8,
+                     device="cuda")
+    rc = lib.kd_chunked_kl_fwd_bwd(h.data_ptr(), W.data_ptr(), kd.KD_F32, idx.data_ptr(),
+                                   p.data_ptr(), mask.data_ptr(), 64, 32, 500, 4, 32,
+                                   loss.data_ptr(), dh.data_ptr(), dW.data_ptr(), None, None,
+                                   None, ws.data_ptr(), ws.numel(),
+                                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 2, lib.kd_last_error()
+    assert bool((loss == 7.0).all() and (dh == 7.0).all() and (dW == 7.0).all())
+
+
+def test_gradient_invariants_on_gpu(torch_cuda):
+    """sum_v dW[v, :] = 0; a constant column of W gives a zero column of dh;
+    <dh, h> = <dW, W>."""
+    inp = synth.make(1, seed=15, N=300, d=64, V=4000, K=10, chunk=128, dtype="f32")
+    inp.W[:, 5] = 0.25
+    got = run(inp, torch_cuda)
+    scale = np.abs(got["dW"]).max()
+    assert np.abs(got["dW"].sum(0)).max() < 1e-4 * scale * np.sqrt(4000)
+    assert np.abs(got["dh"][:, 5]).max() < 1e-4 * np.abs(got["dh"]).max()
+    a = float(np.sum(got["dh"] * inp.h64()))
+    b = float(np.sum(got["dW"] * inp.W64()))
+    assert abs(a - b) <= 1e-4 * max(abs(a), abs(b))
+
+
+# ------------------------------------------------------------------ full-size workloads
+_CACHE = {}
+
+
+def _full(cid):
+    if cid not in _CACHE:
+        _CACHE.clear()
+        _CACHE[cid] = synth.make(cid)
+    return _CACHE[cid]
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_full_size_workload_on_sampled_rows(torch_cuda, cid):
+    torch = torch_cuda
+    inp = _full(cid)
+    cfg = inp.cfg
+    print(f"config {cid} {cfg.name}: N={cfg.N} d={cfg.d} V={cfg.V} K={cfg.K} chunk={cfg.chunk}",
+          flush=True)
+    raw = run_raw(inp, torch, rows=True)
+    rows = synth.subset_rows(cfg, inp.seed, 512)
+    sel = torch.from_numpy(rows).cuda()
+    got = {k: to_f64(raw[k], torch) for k in ("loss", "row_loss", "row_lse", "zg")}
+    got["dh"] = to_f64(raw["dh"].index_select(0, sel), torch)
+    dh_masked_zero = bool((raw["dh"][torch.from_numpy(inp.mask == 0).cuda()] == 0).all())
+    del raw
+    count = int((inp.mask != 0).sum())
+    # the mean loss is the masked mean of the per-row losses the GPU returns
+    assert rel(got["loss"][0], got["row_loss"].sum() / count) < 1e-5
+    ref = oracle.rows_forward_backward(inp.h64(rows), inp.W64(), inp.idx[rows], inp.p[rows],
+                                       inp.mask[rows], count)
+    tol = TOL[cfg.dtype]
+    errs = dict(row_loss=rel_fro(got["row_loss"][rows], ref["row_loss"]),
+                row_lse=max_abs_rel(got["row_lse"][rows], ref["row_lse"]),
+                zg=rel_fro(got["zg"][rows], ref["zg"]),
+                dh=rel_fro(got["dh"], ref["dh"]))
+    print(f"config {cid} sampled rows:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert errs["row_loss"] <= tol["loss"], errs
+    assert errs["row_lse"] <= tol["loss"], errs
+    assert errs["zg"] <= tol["grad"], errs
+    assert errs["dh"] <= tol["grad"], errs
+    assert dh_masked_zero
+    del got
+    # dW (and the loss) of a 512-row sub-batch through the same kernels, over two chunks
+    sub = synth.take_rows(inp, rows)
+    gs = run(sub, torch, chunk=256, rows=True)
+    ref = oracle.forward_backward(sub.h64(), sub.W64(), sub.idx, sub.p, sub.mask)
+    errs = dict(loss=rel(gs["loss"][0], ref["loss"]), dW=rel_fro(gs["dW"], ref["dW"]),
+                dh=rel_fro(gs["dh"], ref["dh"]))
+    print(f"config {cid} sub-batch:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert errs["loss"] <= tol["loss"], errs
+    assert errs["dW"] <= tol["grad"], errs
+    assert errs["dh"] <= tol["grad"], errs
