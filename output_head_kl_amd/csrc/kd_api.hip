@@ -66,7 +66,7 @@ int check_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32
   if (chunk < 1) return fail(KD_E_ARG, "chunk = %lld < 1", (long long)chunk);
   if (K > 65536) return fail(KD_E_UNSUPPORTED, "K = %d above 65536", K);
   if (d % 8 != 0) return fail(KD_E_UNSUPPORTED, "d = %lld is not a multiple of 8", (long long)d);
-  if (d > (1 << 20) || V > (int64_t)1 << 30)
+  if (d > (1 << 20) || V > ((int64_t)1 << 24))
     return fail(KD_E_UNSUPPORTED, "d or V too large");
   const int64_t lim = (int64_t)1 << 62;
   if (N > 0 && (N > lim / d || N > lim / K)) return fail(KD_E_ARG, "N too large");

@@ -426,13 +426,271 @@ struct EpiDw {
   }
 };
 
+// ---------------------------------------------------------------------------------
+// bf16 MFMA GEMM core, pipelined
+//
+// Same tile, wave layout, operand kinds and epilogues as gemm_kernel, with:
+//  * operands copied global -> LDS by the buffer unit (buffer_load_dwordx4 ... lds),
+//    so no staging registers; lanes whose element lies outside the operand get an
+//    offset past the buffer's range and read zero;
+//  * a ring of NST LDS stages of BK k, every slot loading: the slot of the stage just
+//    consumed is refilled at once, NST stages ahead;
+//  * one barrier per stage, placed before the last 16-k substep, so that the fragment
+//    reads for the next substep always overlap 16 MFMAs in flight.
+// KC stage tile: [256 rows][2*BK B], 16-B chunk kc of row r at kc ^ swz(r).
+// MC stage tile: [BK k][512 B], 16-B chunk mc of row k at chunk mc ^ ((k&3)<<2).
+// The LDS serves 256 B per clock (64 banks of 4 B): a ds_read_b128 in four phases of
+// 16 lanes, a ds_read_b64_tr_b16 in two phases of 32 lanes.  With these swizzles
+// every phase of a fragment read touches 16 distinct 16-B bank groups.
+// ---------------------------------------------------------------------------------
+namespace pipe {
+constexpr int OOB = (int)0x80000000;   // offset outside every buffer: reads zero
+
+// Stage geometry for a k-depth of BK bf16 (32 or 64).
+template <int BK> struct Geo {
+  static constexpr int OPB = 256 * BK * 2;   // bytes per operand per stage
+  static constexpr int STAGE = 2 * OPB;
+  static constexpr int ROWB = BK * 2;        // KC row bytes
+  static constexpr int CPR = BK / 8;         // KC 16-B chunks per row
+  static constexpr int NI = BK / 8;          // buffer loads per wave per operand per stage
+  // KC swizzle: a 16-lane LDS phase reads 16 rows of one logical chunk; rows that share
+  // a 256-B bank window (same row % (256/ROWB)) get distinct chunks.
+  static __device__ __forceinline__ int kc_swz(int row) {
+    return BK == 32 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+  }
+};
+
+// Per-lane description of the chunks (of 16 B) one lane moves per operand per stage.
+template <int BK> struct LaneChunks {
+  int rel[Geo<BK>::NI];   // byte offset relative to the operand base of the stage
+  int mn[Geo<BK>::NI];    // mn offset of the chunk within the tile
+  int k[Geo<BK>::NI];     // k offset of the chunk within the stage
+};
+
+template <int KIND, int BK>
+__device__ __forceinline__ LaneChunks<BK> lane_chunks(long long ld, int w, int lane) {
+  using GG = Geo<BK>;
+  LaneChunks<BK> c;
+#pragma unroll
+  for (int j = 0; j < GG::NI; ++j) {
+    const int q = (w * GG::NI + j) * 64 + lane;   // chunk position in LDS (16 B units)
+    if (KIND == OP_KC) {
+      const int row = q / GG::CPR, kc = (q % GG::CPR) ^ GG::kc_swz(row);
+      c.mn[j] = row;
+      c.k[j] = kc * 8;
+      c.rel[j] = (int)(((long long)row * ld + kc * 8) * 2);
+    } else {
+      const int k = q >> 5, mc = (q & 31) ^ ((k & 3) << 2);
+      c.mn[j] = mc * 8;
+      c.k[j] = k;
+      c.rel[j] = (int)(((long long)k * ld + mc * 8) * 2);
+    }
+  }
+  return c;
+}
+
+template <int KIND, int BK> struct Loader {
+static __device__ __forceinline__ void issue(const Operand &op, const LaneChunks<BK> &c, int mn0,
+                                             int k0, char *lds, int w) {
+  using GG = Geo<BK>;
+  const unsigned short *base = (const unsigned short *)op.ptr;
+  base += KIND == OP_KC ? (long long)mn0 * op.ld + k0 : (long long)k0 * op.ld + mn0;
+  __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < GG::NI; ++j) {
+    const bool ok = (mn0 + c.mn[j] < op.mn_ext) && (k0 + c.k[j] < op.k_ext);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (LDS_AS void *)((LDS_AS char *)lds + (w * GG::NI + j) * 1024), 16,
+        ok ? c.rel[j] : OOB, 0, 0, 0);
+  }
+}
+};
+
+template <int KIND, int BK> struct PFrag;
+template <int BK> struct PFrag<OP_KC, BK> {
+  static __device__ __forceinline__ bf16x8 load(const char *lds, int r0, int ks, int lane) {
+    using GG = Geo<BK>;
+    const int row = r0 + (lane & 31), kc = ks * 2 + (lane >> 5);
+    return *(const LDS_AS bf16x8 *)((const LDS_AS char *)lds + row * GG::ROWB +
+                                    ((kc ^ GG::kc_swz(row)) << 4));
+  }
+};
+template <int BK> struct PFrag<OP_MC, BK> {
+  static __device__ __forceinline__ bf16x8 load(const char *lds, int r0, int ks, int lane) {
+    const int s = lane & 15, g = lane >> 4;
+    const int m = r0 + (g & 1) * 16 + 4 * (s & 3);
+    const int k = ks * 16 + (g >> 1) * 8 + (s >> 2);
+    const int col = (((m >> 3) ^ ((k & 3) << 2)) << 4) + (m & 7) * 2;
+    const LDS_AS char *b = (const LDS_AS char *)lds;
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(b + k * 512 + col));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(b + (k + 4) * 512 + col));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
+// s_waitcnt with vmcnt <= n (n a multiple of 8, at most 56) and, with LGKM0, lgkmcnt == 0.
+// Immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <bool LGKM0>
+__device__ __forceinline__ void wait_vm(int n) {
+  constexpr int base = LGKM0 ? 0x0070 : 0x0F70;
+  switch (n >= 56 ? 7 : n / 8) {
+    case 0: __builtin_amdgcn_s_waitcnt(base | 0x0); break;
+    case 1: __builtin_amdgcn_s_waitcnt(base | 0x8); break;
+    case 2: __builtin_amdgcn_s_waitcnt(base | 0x4000); break;
+    case 3: __builtin_amdgcn_s_waitcnt(base | 0x4008); break;
+    case 4: __builtin_amdgcn_s_waitcnt(base | 0x8000); break;
+    case 5: __builtin_amdgcn_s_waitcnt(base | 0x8008); break;
+    case 6: __builtin_amdgcn_s_waitcnt(base | 0xC000); break;
+    default: __builtin_amdgcn_s_waitcnt(base | 0xC008); break;
+  }
+}
+}  // namespace pipe
+
+// Scheduling hints: sched_group_barrier(mask, n, id) asks the scheduler for the next
+// n instructions of a class; the sequence below places one load or LDS read in the
+// shadow of each MFMA, so that with one wave per SIMD the matrix core never waits for
+// the wave to issue its memory traffic.
+#define KD_SG_MFMA 0x008
+#define KD_SG_VALU 0x002
+#define KD_SG_SALU 0x004
+#define KD_SG_VMEM 0x020
+#define KD_SG_DSRD 0x100
+
+template <int AK, int BKIND, class Epi, int NST = 5, int BK = 32>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
+  using namespace pipe;
+  using GG = Geo<BK>;
+  constexpr int S = BK / 16;            // 16-k substeps per stage
+  constexpr int LPS = 2 * GG::NI;       // buffer loads per wave per stage
+  // LDS reads per substep: 4 fragments per operand, 2 transposed reads per MC fragment
+  constexpr int NRD = 4 * (AK == OP_MC ? 2 : 1) + 4 * (BKIND == OP_MC ? 2 : 1);
+  __shared__ __attribute__((aligned(1024))) char smem[NST * GG::STAGE];
+
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_split = G.ntm * G.ntn;
+  const int split = lin / per_split;
+  const int rem = lin - split * per_split;
+  int tm, tn;
+  if (G.order == 0) {
+    tm = rem / G.ntn;
+    tn = rem - tm * G.ntn;
+  } else {
+    tn = rem / G.ntm;
+    tm = rem - tn * G.ntm;
+  }
+  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int kb = split * G.k_len;
+  const int ke = min(G.k_total, kb + G.k_len);
+  const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wr = w >> 1, wc = w & 1;
+  const LaneChunks<BK> ca = lane_chunks<AK, BK>(A.ld, w, lane);
+  const LaneChunks<BK> cb = lane_chunks<BKIND, BK>(B.ld, w, lane);
+  // k beyond this split's range reads zero (and moves no data)
+  Operand Ak = A, Bk = B;
+  Ak.k_ext = min(A.k_ext, ke);
+  Bk.k_ext = min(B.k_ext, ke);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  // Prologue: every slot loading (stages past the end are all-zero loads, so the
+  // count of loads in flight is the same in every iteration); stage 0 landed.
+  for (int s = 0; s < NST; ++s) {
+    Loader<AK, BK>::issue(Ak, ca, m0, kb + s * BK, smem + s * GG::STAGE, w);
+    Loader<BKIND, BK>::issue(Bk, cb, n0, kb + s * BK, smem + s * GG::STAGE + GG::OPB, w);
+  }
+  wait_vm<false>(LPS * (NST - 1));
+  __syncthreads();
+
+  bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[0][i] = PFrag<AK, BK>::load(smem, wr * 128 + i * 32, 0, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[0][j] = PFrag<BKIND, BK>::load(smem + GG::OPB, wc * 128 + j * 32, 0, lane);
+
+  int bcur = 0;  // ring slot of stage it
+  for (int it = 0; it < nk; ++it) {
+    const int bnext = bcur + 1 == NST ? 0 : bcur + 1;
+    char *cur = smem + bcur * GG::STAGE;
+#pragma unroll
+    for (int ss = 0; ss < S - 1; ++ss) {
+      // substep ss on registers [ss&1]; read substep ss+1 meanwhile
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[(ss + 1) & 1][i] = PFrag<AK, BK>::load(cur, wr * 128 + i * 32, ss + 1, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[(ss + 1) & 1][j] = PFrag<BKIND, BK>::load(cur + GG::OPB, wc * 128 + j * 32, ss + 1, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma(fa[ss & 1][i], fb[ss & 1][j], acc[i][j]);
+#pragma unroll
+      for (int q = 0; q < NRD; ++q) {
+        __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(KD_SG_DSRD, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 16 - NRD < 0 ? 0 : 16 - NRD, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Stage it+1 must have landed for every wave, and every wave must hold the whole of
+    // stage it in registers or accumulators, since its slot is refilled next.
+    wait_vm<true>(LPS * (NST - 2));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // last substep on registers [(S-1)&1]; meanwhile read substep 0 of stage it+1 and
+    // refill this slot with stage it+NST
+    const char *nx = smem + bnext * GG::STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = PFrag<AK, BK>::load(nx, wr * 128 + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[0][j] = PFrag<BKIND, BK>::load(nx + GG::OPB, wc * 128 + j * 32, 0, lane);
+    Loader<AK, BK>::issue(Ak, ca, m0, kb + (it + NST) * BK, cur, w);
+    Loader<BKIND, BK>::issue(Bk, cb, n0, kb + (it + NST) * BK, cur + GG::OPB, w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma(fa[(S - 1) & 1][i], fb[(S - 1) & 1][j], acc[i][j]);
+    // reads for the next stage first (they gate the next iteration), loads after
+#pragma unroll
+    for (int q = 0; q < (NRD < 8 ? NRD : 8); ++q) {
+      __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(KD_SG_DSRD, NRD > 8 ? 2 : 1, 1);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM, LPS / 8, 1);
+      __builtin_amdgcn_sched_group_barrier(KD_SG_VALU, 2, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bcur = bnext;
+  }
+  wait_vm<false>(0);  // the zero loads issued past the end
+  epi(acc, m0 + wr * 128, n0 + wc * 128, lane, split);
+}
+
 template <int DT, int AK, int BKIND, class Epi>
 static hipError_t run_gemm(const Operand &A, const Operand &B, const GemmGrid &G, const Epi &epi,
                            hipStream_t s) {
   const long long T = (long long)G.ntm * G.ntn * G.nsplit;
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<DT, AK, BKIND, Epi>), dim3((unsigned)T), dim3(256), 0, s, A,
-                     B, G, epi);
+  if (DT == 1)
+    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKIND, Epi>), dim3((unsigned)T), dim3(256), 0, s, A,
+                       B, G, epi);
+  else
+    hipLaunchKernelGGL((gemm_kernel<DT, AK, BKIND, Epi>), dim3((unsigned)T), dim3(256), 0, s, A,
+                       B, G, epi);
   return hipGetLastError();
 }
 
