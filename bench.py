@@ -37,6 +37,9 @@ def parse():
                     help="token rows of the workload timed through the CPU oracle")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip per-kernel HIP-event timing inside the timed region")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="after the run, launch one plain device copy of this many GiB "
+                         "(a kernel of known traffic, for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -186,6 +189,15 @@ def main():
         "kernels": kernels,
         "cpu_baseline": None,
     }
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * 2**30) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_bytes_each_way"] = n * 4
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)

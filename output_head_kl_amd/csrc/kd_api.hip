@@ -106,13 +106,12 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->n_lse = (V + kLseRows - 1) / kLseRows;
   // Split the vocabulary of the dh GEMM so that about three workgroups per CU run.
   const int64_t tiles = (L->d_pad / kTile) * (L->C_alloc / kTile);
-  const int64_t kstep = dtype == KD_BF16 ? 64 : 32;
   int64_t ns = (768 + tiles - 1) / tiles;
-  const int64_t max_by_k = L->V_pad / (8 * kstep);  // at least 8 k-steps per split
+  const int64_t max_by_k = L->V_pad / kTile;  // at least one dz column block per split
   if (ns > max_by_k) ns = max_by_k;
   if (ns > 16) ns = 16;
   if (ns < 1) ns = 1;
-  L->k_split = rup((L->V_pad + ns - 1) / ns, kstep);
+  L->k_split = rup((L->V_pad + ns - 1) / ns, kTile);  // splits start on a dz column block
   L->nsplit = (int)((L->V_pad + L->k_split - 1) / L->k_split);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -241,15 +240,17 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
     if (count == 0) continue;  // forward-only sweep for the per-row outputs
     LAUNCH(kd::KC_MISC, kd::launch_accum_loss(rowterm, rows, acc, stream));
     LAUNCH(kd::KC_BWD_GEMM,
-           kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse, sM, dz, L.V_pad, stream));
+           kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse, sM, dz, L.V_pad, L.C_alloc,
+                               stream));
     LAUNCH(kd::KC_SCATTER,
-           kd::launch_scatter(dtype, dz, L.V_pad, idx_c, p_c, srow, rows, K, stream));
+           kd::launch_scatter(dtype, dz, L.C_alloc, idx_c, p_c, srow, rows, K, stream));
     LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, rows, d, V, L.V_pad, L.nsplit,
                                               L.k_split, dhpart, L.d_pad, L.C_alloc, stream));
     LAUNCH(kd::KC_DH_REDUCE, kd::launch_dh_reduce(dtype, dhpart, L.nsplit, L.C_alloc, L.d_pad,
                                                   rows, d, (char *)dh + c0 * d * es, stream));
     LAUNCH(kd::KC_DW_GEMM,
-           kd::launch_dw_gemm(dtype, dz, h_c, rows, d, V, L.V_pad, dW, chunk_i > 0, stream));
+           kd::launch_dw_gemm(dtype, dz, h_c, rows, d, V, L.V_pad, L.C_alloc, dW, chunk_i > 0,
+                              stream));
   }
   if (count > 0) LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));
   return KD_OK;

@@ -32,11 +32,11 @@ enum KClass {
 struct Layout {
   int64_t C;          // token rows per chunk (min(chunk, N))
   int64_t C_alloc;    // C rounded up to the tile
-  int64_t V_pad;      // V rounded up to the tile (row pitch of dz)
+  int64_t V_pad;      // V rounded up to the tile (dz holds V_pad / 256 column blocks)
   int64_t d_pad;      // d rounded up to the tile (row pitch of the dh partials)
   int64_t n_lse;      // ceil(V / kLseRows)
   int nsplit;         // vocabulary splits of the dh GEMM
-  int64_t k_split;    // vocabulary rows per split (multiple of the k-step)
+  int64_t k_split;    // vocabulary rows per split (a multiple of 256)
   size_t off_flags, off_acc, off_partials, off_lse, off_sM, off_s, off_rowterm, off_zg,
       off_dz, off_dhpart, total;
 };
@@ -61,10 +61,12 @@ hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part
                           hipStream_t s);
 hipError_t launch_accum_loss(const double *rowterm, int64_t rows, double *acc, hipStream_t s);
 hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s);
+// dz is stored as blocks of 256 vocabulary columns: element (c, v) at
+// dz[(v / 256) * C_alloc * 256 + c * 256 + v % 256].
 hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
                            int64_t V, const float *lse, const float *sM, void *dz,
-                           int64_t V_pad, hipStream_t s);
-hipError_t launch_scatter(int dtype, void *dz, int64_t V_pad, const int32_t *idx_c,
+                           int64_t V_pad, int64_t C_alloc, hipStream_t s);
+hipError_t launch_scatter(int dtype, void *dz, int64_t C_alloc, const int32_t *idx_c,
                           const float *p_c, const float *srow, int64_t rows, int32_t K,
                           hipStream_t s);
 hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, int64_t rows, int64_t d,
@@ -73,7 +75,7 @@ hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, int64_t rows
 hipError_t launch_dh_reduce(int dtype, const float *part, int nsplit, int64_t C_alloc,
                             int64_t d_pad, int64_t rows, int64_t d, void *dh, hipStream_t s);
 hipError_t launch_dw_gemm(int dtype, const void *dz, const void *h_c, int64_t rows, int64_t d,
-                          int64_t V, int64_t V_pad, float *dW, int accumulate,
+                          int64_t V, int64_t V_pad, int64_t C_alloc, float *dW, int accumulate,
                           hipStream_t s);
 
 // --- timing hooks (kd_api.hip) ---

@@ -90,12 +90,22 @@ __device__ __forceinline__ int xcd_remap(int bid, int T) {
 // ---------------------------------------------------------------------------------
 enum { OP_KC = 0, OP_MC = 1 };
 
+// Element (mn, k) of an operand lives at
+//   KC: ptr[(k / 256) * ts + k % 256 + mn * ld],  MC: ptr[(mn / 256) * ts + mn % 256 + k * ld].
+// A plain row-major matrix has ts = 256; a matrix stored as blocks of 256 contiguous
+// columns (each block [rows][256]) has ld = 256 and ts = rows * 256.
 struct Operand {
-  const void *ptr;  // element (mn, k) at KC: ptr[mn*ld + k], MC: ptr[k*ld + mn]
-  long long ld;     // elements
+  const void *ptr;
+  long long ld;     // elements between rows
   int mn_ext;       // rows/cols with mn >= mn_ext read as zero
   int k_ext;        // k >= k_ext read as zero
+  long long ts;     // elements between 256-column blocks
 };
+
+__device__ __forceinline__ long long op_index(const Operand &op, int kind, int mn, int k) {
+  return kind == 0 ? (long long)(k >> 8) * op.ts + (k & 255) + (long long)mn * op.ld
+                   : (long long)(mn >> 8) * op.ts + (mn & 255) + (long long)k * op.ld;
+}
 
 struct GemmGrid {
   int ntm, ntn, nsplit;
@@ -136,7 +146,7 @@ __device__ __forceinline__ void load_stage(u32x4 (&r)[8], const Operand &op, int
       mn = mn0 + (q & 63) * CH;
     }
     const bool ok = mn < op.mn_ext && k < op.k_ext;
-    const long long e = KIND == OP_KC ? (long long)mn * op.ld + k : (long long)k * op.ld + mn;
+    const long long e = op_index(op, KIND, mn, k);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (ok) v = *(const u32x4 *)(base + e * ES);
     r[i] = v;
@@ -340,8 +350,8 @@ struct EpiFwdLse {
 // Backward: dz[c][v] = sM[c] * exp(z - lse[c]) for v < V, 0 for V <= v < V_pad.
 template <int DT>
 struct EpiBwdDz {
-  void *dz;
-  long long ld;  // V_pad
+  void *dz;      // blocks of 256 vocabulary columns: [V_pad/256][C_alloc][256]
+  long long ts;  // C_alloc * 256
   const float *lse, *sM;
   int V, rows;
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
@@ -364,9 +374,10 @@ struct EpiBwdDz {
             x[e] = (v0 + e < V) ? a * fast_exp2(fmaf(acc[rb][cb][g * 4 + e], kLog2e, -l2)) : 0.f;
           if (DT == 1) {
             u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-            *(u32x2 *)((unsigned short *)dz + (long long)c * ld + v0) = pk;
+            *(u32x2 *)((unsigned short *)dz + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) = pk;
           } else {
-            *(f32x4 *)((float *)dz + (long long)c * ld + v0) = f32x4{x[0], x[1], x[2], x[3]};
+            *(f32x4 *)((float *)dz + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) =
+                f32x4{x[0], x[1], x[2], x[3]};
           }
         }
     }
@@ -399,28 +410,32 @@ struct EpiDhPart {
   }
 };
 
-// dW: tile rows are hidden units j, columns vocabulary entries v.
+// dW: tile rows are vocabulary entries v, columns hidden units j, so each accumulator
+// register holds 32 consecutive floats of two dW rows (one per half-wave).  The first
+// chunk stores; later chunks add with one fire-and-forget atomic per element, so the
+// workgroup does not wait for dW to be read back and the result does not depend on
+// timing (each element gets exactly one addition per launch, launches are ordered).
 struct EpiDw {
   float *dW;
   int d, V, accumulate;
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
                                              int) const {
-    const int jl = m0 + (lane >> 5) * 4;
+    const int vl = m0 + (lane >> 5) * 4;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const int v = n0 + cb * 32 + (lane & 31);
-      if (v >= V) continue;
+      const int j = n0 + cb * 32 + (lane & 31);
+      if (j >= d) continue;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int j = jl + rb * 32 + g * 8;
-          if (j >= d) continue;
-          f32x4 x = {acc[rb][cb][g * 4], acc[rb][cb][g * 4 + 1], acc[rb][cb][g * 4 + 2],
-                     acc[rb][cb][g * 4 + 3]};
-          f32x4 *p = (f32x4 *)(dW + (long long)v * d + j);
-          if (accumulate) x += *p;
-          *p = x;
+        for (int i = 0; i < 16; ++i) {
+          const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
+          if (v >= V) continue;
+          float *p = dW + (long long)v * d + j;
+          if (accumulate)
+            unsafeAtomicAdd(p, acc[rb][cb][i]);
+          else
+            *p = acc[rb][cb][i];
         }
     }
   }
@@ -494,7 +509,7 @@ static __device__ __forceinline__ void issue(const Operand &op, const LaneChunks
                                              int k0, char *lds, int w) {
   using GG = Geo<BK>;
   const unsigned short *base = (const unsigned short *)op.ptr;
-  base += KIND == OP_KC ? (long long)mn0 * op.ld + k0 : (long long)k0 * op.ld + mn0;
+  base += op_index(op, KIND, mn0, k0);   // a stage never crosses a 256-column block
   __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
@@ -701,8 +716,8 @@ static inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b)
 // ---------------------------------------------------------------------------------
 hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
                            int64_t V, float2 *partials, int64_t ld_part, hipStream_t s) {
-  Operand A{W, d, (int)V, (int)d};
-  Operand B{h_c, d, (int)rows, (int)d};
+  Operand A{W, d, (int)V, (int)d, 256};
+  Operand B{h_c, d, (int)rows, (int)d, 256};
   GemmGrid G{cdiv(V, kTile), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
   EpiFwdLse e{partials, ld_part, (int)V, (int)rows};
   return dtype == 1 ? run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s)
@@ -711,15 +726,15 @@ hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
 
 hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
                            int64_t V, const float *lse, const float *sM, void *dz,
-                           int64_t V_pad, hipStream_t s) {
-  Operand A{W, d, (int)V, (int)d};
-  Operand B{h_c, d, (int)rows, (int)d};
+                           int64_t V_pad, int64_t C_alloc, hipStream_t s) {
+  Operand A{W, d, (int)V, (int)d, 256};
+  Operand B{h_c, d, (int)rows, (int)d, 256};
   GemmGrid G{cdiv(V, kTile), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
   if (dtype == 1) {
-    EpiBwdDz<1> e{dz, V_pad, lse, sM, (int)V, (int)rows};
+    EpiBwdDz<1> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows};
     return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
   }
-  EpiBwdDz<0> e{dz, V_pad, lse, sM, (int)V, (int)rows};
+  EpiBwdDz<0> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows};
   return run_gemm<0, OP_KC, OP_KC>(A, B, G, e, s);
 }
 
@@ -727,8 +742,8 @@ hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, int64_t rows
                           int64_t V, int64_t V_pad, int nsplit, int64_t k_split, float *part,
                           int64_t d_pad, int64_t C_alloc, hipStream_t s) {
   // D[j][c] = sum_v W[v][j] dz[c][v]: A = W as MC ([v][j]), B = dz as KC ([c][v]).
-  Operand A{W, d, (int)d, (int)V};
-  Operand B{dz, V_pad, (int)rows, (int)V_pad};
+  Operand A{W, d, (int)d, (int)V, 256};
+  Operand B{dz, 256, (int)rows, (int)V_pad, C_alloc * 256};
   GemmGrid G{cdiv(d, kTile), cdiv(rows, kTile), nsplit, (int)k_split, (int)V_pad, 0};
   EpiDhPart e{part, C_alloc * d_pad, d_pad, (int)rows};
   return dtype == 1 ? run_gemm<1, OP_MC, OP_KC>(A, B, G, e, s)
@@ -736,11 +751,12 @@ hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, int64_t rows
 }
 
 hipError_t launch_dw_gemm(int dtype, const void *dz, const void *h_c, int64_t rows, int64_t d,
-                          int64_t V, int64_t V_pad, float *dW, int accumulate, hipStream_t s) {
-  // D[j][v] = sum_c h[c][j] dz[c][v]: A = h as MC ([c][j]), B = dz as MC ([c][v]).
-  Operand A{h_c, d, (int)d, (int)rows};
-  Operand B{dz, V_pad, (int)V_pad, (int)rows};
-  GemmGrid G{cdiv(d, kTile), cdiv(V, kTile), 1, (int)rows, (int)rows, 1};
+                          int64_t V, int64_t V_pad, int64_t C_alloc, float *dW, int accumulate,
+                          hipStream_t s) {
+  // D[v][j] = sum_c dz[c][v] h[c][j]: A = dz as MC ([c][v]), B = h as MC ([c][j]).
+  Operand A{dz, 256, (int)V_pad, (int)rows, C_alloc * 256};
+  Operand B{h_c, d, (int)d, (int)rows, 256};
+  GemmGrid G{cdiv(V, kTile), cdiv(d, kTile), 1, (int)rows, (int)rows, 0};
   EpiDw e{dW, (int)d, (int)V, accumulate};
   return dtype == 1 ? run_gemm<1, OP_MC, OP_MC>(A, B, G, e, s)
                     : run_gemm<0, OP_MC, OP_MC>(A, B, G, e, s);
@@ -975,7 +991,7 @@ hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStr
 // The first entry of each distinct index does the update, so no two threads touch
 // the same element.
 template <int DT>
-__global__ void k_scatter(void *dz, long long ld, const int32_t *idx, const float *p,
+__global__ void k_scatter(void *dz, long long ts, const int32_t *idx, const float *p,
                           const float *srow, int rows, int K) {
   const long long g = blockIdx.x * (long long)blockDim.x + threadIdx.x;
   if (g >= (long long)rows * K) return;
@@ -991,24 +1007,24 @@ __global__ void k_scatter(void *dz, long long ld, const int32_t *idx, const floa
   for (int j = k + 1; j < K; ++j)
     if (ir[j] == v) tot += pr[j];
   if (DT == 1) {
-    unsigned short *q = (unsigned short *)dz + (long long)r * ld + v;
+    unsigned short *q = (unsigned short *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
     *q = f32_to_bf16(bf16_to_f32(*q) - sr * tot);
   } else {
-    float *q = (float *)dz + (long long)r * ld + v;
+    float *q = (float *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
     *q = *q - sr * tot;
   }
 }
 
-hipError_t launch_scatter(int dtype, void *dz, int64_t V_pad, const int32_t *idx_c,
+hipError_t launch_scatter(int dtype, void *dz, int64_t C_alloc, const int32_t *idx_c,
                           const float *p_c, const float *srow, int64_t rows, int32_t K,
                           hipStream_t s) {
   const long long n = rows * (long long)K;
   const int blocks = (int)((n + 255) / 256);
   if (dtype == 1)
-    hipLaunchKernelGGL(k_scatter<1>, dim3(blocks), dim3(256), 0, s, dz, (long long)V_pad, idx_c,
+    hipLaunchKernelGGL(k_scatter<1>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256, idx_c,
                        p_c, srow, (int)rows, (int)K);
   else
-    hipLaunchKernelGGL(k_scatter<0>, dim3(blocks), dim3(256), 0, s, dz, (long long)V_pad, idx_c,
+    hipLaunchKernelGGL(k_scatter<0>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256, idx_c,
                        p_c, srow, (int)rows, (int)K);
   return hipGetLastError();
 }
