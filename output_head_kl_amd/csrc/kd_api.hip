@@ -40,7 +40,7 @@ Prof g_prof;
 std::mutex g_prof_mu;
 
 const char *const kClassNames[kd::KC_COUNT] = {
-    "validate", "fwd_gemm_lse", "gather", "combine_lse_loss", "bwd_gemm_dz",
+    "validate", "fwd_gemm_lse", "bucket", "combine_lse_loss", "bwd_gemm_dz",
     "scatter",  "dh_gemm",      "dh_reduce", "dw_gemm",      "misc"};
 
 #define HIPCHK(expr)                                                                 \
@@ -129,6 +129,11 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->off_zg = take((size_t)L->C_alloc * K * 4);
   L->off_dz = take((size_t)L->C_alloc * L->V_pad * es);
   L->off_dhpart = take((size_t)L->nsplit * L->C_alloc * L->d_pad * 4);
+  L->nkeys = (V + kTile - 1) / kTile * (L->C_alloc / kTile);
+  L->off_bcount = take((size_t)L->nkeys * 4);
+  L->off_bcursor = take((size_t)L->nkeys * 4);
+  L->off_boff = take((size_t)(L->nkeys + 1) * 4);
+  L->off_bent = take((size_t)L->C_alloc * K * 4);
   L->total = off;
   return true;
 }
@@ -189,6 +194,10 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
   float *zg_ws = (float *)(ws + L.off_zg);
   void *dz = ws + L.off_dz;
   float *dhpart = (float *)(ws + L.off_dhpart);
+  int *bcount = (int *)(ws + L.off_bcount);
+  int *bcursor = (int *)(ws + L.off_bcursor);
+  int *boff = (int *)(ws + L.off_boff);
+  unsigned *bent = (unsigned *)(ws + L.off_bent);
   const int64_t es = dtype == KD_BF16 ? 2 : 4;
 
   if (N == 0) {
@@ -220,6 +229,7 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
     if (!want_rows) return KD_OK;
   }
   const float inv_count = count > 0 ? (float)(1.0 / (double)count) : 0.f;
+  LAUNCH(kd::KC_MISC, kd::launch_fill_zero(bcount, (size_t)L.nkeys * 4, stream));
 
   int chunk_i = 0;
   for (int64_t c0 = 0; c0 < N; c0 += L.C, ++chunk_i) {
@@ -230,9 +240,10 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
     const uint8_t *mask_c = loss_mask ? loss_mask + c0 : nullptr;
     float *zg_c = zg ? zg + c0 * K : zg_ws;
 
-    LAUNCH(kd::KC_FWD_GEMM,
-           kd::launch_fwd_gemm(dtype, W, h_c, rows, d, V, partials, L.C_alloc, stream));
-    LAUNCH(kd::KC_GATHER, kd::launch_gather(dtype, h_c, W, idx_c, rows, d, K, zg_c, stream));
+    LAUNCH(kd::KC_BUCKET,
+           kd::launch_buckets(idx_c, rows, K, V, bcount, bcursor, boff, bent, stream));
+    LAUNCH(kd::KC_FWD_GEMM, kd::launch_fwd_gemm(dtype, W, h_c, rows, d, V, partials, L.C_alloc,
+                                                boff, bent, zg_c, K, stream));
     LAUNCH(kd::KC_COMBINE,
            kd::launch_combine(partials, L.n_lse, L.C_alloc, zg_c, p_c, mask_c, rows, K, inv_count,
                               lse, sM, srow, rowterm, row_loss ? row_loss + c0 : nullptr,

@@ -17,7 +17,7 @@ constexpr int kLseRows = 128;
 enum KClass {
   KC_VALIDATE = 0,
   KC_FWD_GEMM,     // logits GEMM + per-tile max / sum-exp
-  KC_GATHER,       // logits at the teacher's indices
+  KC_BUCKET,       // teacher hits sorted by output tile (for the fused gather)
   KC_COMBINE,      // logsumexp + per-token loss
   KC_BWD_GEMM,     // logits recomputed + dense dz
   KC_SCATTER,      // sparse teacher correction of dz
@@ -37,8 +37,9 @@ struct Layout {
   int64_t n_lse;      // ceil(V / kLseRows)
   int nsplit;         // vocabulary splits of the dh GEMM
   int64_t k_split;    // vocabulary rows per split (a multiple of 256)
+  int64_t nkeys;      // buckets per chunk: ceil(V / 256) * C_alloc / 256
   size_t off_flags, off_acc, off_partials, off_lse, off_sM, off_s, off_rowterm, off_zg,
-      off_dz, off_dhpart, total;
+      off_dz, off_dhpart, off_bcount, off_bcursor, off_boff, off_bent, total;
 };
 
 bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
@@ -49,11 +50,16 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_validate(const int32_t *idx, const float *p, int64_t NK, int64_t V,
                            const uint8_t *mask, int64_t N, int *flags,
                            unsigned long long *count, hipStream_t s);
+// Teacher hits of a chunk sorted by 256 x 256 output tile: offsets[key..key+1) of
+// entries (c_local | v_local << 8 | k << 16), key = (v / 256) * ceil(rows / 256) + c / 256.
+// counts must be zero on entry and are left zero.
+hipError_t launch_buckets(const int32_t *idx_c, int64_t rows, int32_t K, int64_t V, int *counts,
+                          int *cursor, int *offsets, unsigned *entries, hipStream_t s);
+// Logits GEMM with the per-tile (max, sum exp) epilogue and the fused gather into zg.
 hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows,
                            int64_t d, int64_t V, float2 *partials, int64_t ld_part,
+                           const int *boff, const unsigned *bent, float *zg, int32_t K,
                            hipStream_t s);
-hipError_t launch_gather(int dtype, const void *h_c, const void *W, const int32_t *idx_c,
-                         int64_t rows, int64_t d, int32_t K, float *zg, hipStream_t s);
 hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part,
                           const float *zg, const float *p_c, const uint8_t *mask_c,
                           int64_t rows, int32_t K, float inv_count, float *lse, float *sM,

@@ -1,9 +1,10 @@
 // gfx950 kernels of the fused, chunked top-K KL loss.
 //
 // Per token chunk (see kd_api.hip for the sequence):
+//   buckets        the chunk's teacher hits sorted by 256 x 256 output tile;
 //   forward GEMM   z^T tile = W_tile . h_tile^T on MFMA, epilogue: per-token max and
-//                  sum of exp over the tile's vocabulary rows (no logits stored);
-//   gather         z at the teacher's K indices;
+//                  sum of exp over the tile's vocabulary rows, and z gathered at the
+//                  tile's teacher hits (no logits stored);
 //   combine        logsumexp over the tiles, per-token loss;
 //   backward GEMM  z recomputed, epilogue: dz = (mask/count) * M * exp(z - lse), bf16;
 //   scatter        dz -= (mask/count) * p at the teacher's indices;
@@ -303,7 +304,7 @@ void gemm_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
     }
     __syncthreads();
   }
-  epi(acc, m0 + wr * 128, n0 + wc * 128, lane, split);
+  epi(acc, m0 + wr * 128, n0 + wc * 128, lane, split, smem);
 }
 
 // ---------------------------------------------------------------------------------
@@ -311,38 +312,83 @@ void gemm_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
 // ---------------------------------------------------------------------------------
 // Forward: tile rows are vocabulary entries v, columns are tokens c.  Each lane holds
 // 64 of a token's 128 values in the wave's square; lane l^32 holds the rest.
+//  * per (token, 128 vocabulary rows): max and sum of exp(z - max) -> part;
+//  * gather: the tile's teacher hits (bucket key = vocabulary tile * token tiles + token
+//    tile, entries packed c_local | v_local << 8 | k << 16) read z from the tile, staged
+//    through LDS in four slices of 64 vocabulary rows ([256 tokens][68] fp32, 68 KB).
 struct EpiFwdLse {
   float2 *part;   // [n_lse][ld] (max, sum exp(z - max)) per 128 vocabulary rows
   long long ld;
   int V, rows;
+  const int *boff;        // bucket offsets, [ntm * ntn + 1]
+  const unsigned *bent;   // bucket entries
+  int ntn;                // token tiles in the chunk
+  float *zg;              // [rows][K] logits at the teacher's indices
+  int K;
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
-                                             int) const {
-    if (m0 >= V) return;
-    const bool full = m0 + 128 <= V;
-    const int vl = m0 + (lane >> 5) * 4;
+                                             int, char *smem) const {
+    if (m0 < V) {
+      const bool full = m0 + 128 <= V;
+      const int vl = m0 + (lane >> 5) * 4;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      float mx = -INFINITY;
+      for (int cb = 0; cb < 4; ++cb) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
-          if (full || v < V) mx = fmaxf(mx, acc[rb][cb][i]);
+          for (int i = 0; i < 16; ++i) {
+            const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
+            if (full || v < V) mx = fmaxf(mx, acc[rb][cb][i]);
+          }
+        mx = halves_max(mx);
+        const float mx2 = mx * kLog2e;
+        float s = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
+            if (full || v < V) s += fast_exp2(fmaf(acc[rb][cb][i], kLog2e, -mx2));
+          }
+        s = halves_sum(s);
+        const int c = n0 + cb * 32 + (lane & 31);
+        if (lane < 32 && c < rows) part[(long long)(m0 / kLseRows) * ld + c] = make_float2(mx, s);
+      }
+    }
+    // fused gather (the same branch for every wave of the workgroup)
+    const int tm = m0 >> 8, tn = n0 >> 8;
+    const int key = tm * ntn + tn;
+    const int beg = boff[key], end = boff[key + 1];
+    if (beg == end) return;
+    const int t = threadIdx.x, w = t >> 6, wr = w >> 1, wc = w & 1;
+    constexpr int P = 68;
+    const int cl0 = wc * 128 + (lane & 31);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __syncthreads();
+      if (wr == (q >> 1)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rb = (q & 1) * 2 + h;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int vloc = h * 32 + g * 8 + (lane >> 5) * 4;
+              const f32x4 v4 = {acc[rb][cb][g * 4], acc[rb][cb][g * 4 + 1], acc[rb][cb][g * 4 + 2],
+                                acc[rb][cb][g * 4 + 3]};
+              *(LDS_AS f32x4 *)((LDS_AS char *)smem + ((cl0 + cb * 32) * P + vloc) * 4) = v4;
+            }
         }
-      mx = halves_max(mx);
-      const float mx2 = mx * kLog2e;
-      float s = 0.f;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
-          if (full || v < V) s += fast_exp2(fmaf(acc[rb][cb][i], kLog2e, -mx2));
-        }
-      s = halves_sum(s);
-      const int c = n0 + cb * 32 + (lane & 31);
-      if (lane < 32 && c < rows) part[(long long)(m0 / kLseRows) * ld + c] = make_float2(mx, s);
+      }
+      __syncthreads();
+      for (int e = beg + t; e < end; e += 256) {
+        const unsigned ent = bent[e];
+        const int cl = ent & 255, vloc = (ent >> 8) & 255, k = ent >> 16;
+        if ((vloc >> 6) == q)
+          zg[(long long)(tn * 256 + cl) * K + k] =
+              *(const LDS_AS float *)((const LDS_AS char *)smem + (cl * P + (vloc & 63)) * 4);
+      }
     }
   }
 };
@@ -355,7 +401,7 @@ struct EpiBwdDz {
   const float *lse, *sM;
   int V, rows;
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
-                                             int) const {
+                                             int, char *) const {
     const int vl = m0 + (lane >> 5) * 4;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
@@ -390,7 +436,7 @@ struct EpiDhPart {
   long long split_stride, ld;  // C_alloc*d_pad, d_pad
   int rows;
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
-                                             int split) const {
+                                             int split, char *) const {
     float *base = part + split * split_stride;
     const int jl = m0 + (lane >> 5) * 4;
 #pragma unroll
@@ -419,7 +465,7 @@ struct EpiDw {
   float *dW;
   int d, V, accumulate;
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
-                                             int) const {
+                                             int, char *) const {
     const int vl = m0 + (lane >> 5) * 4;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
@@ -692,7 +738,7 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
     bcur = bnext;
   }
   wait_vm<false>(0);  // the zero loads issued past the end
-  epi(acc, m0 + wr * 128, n0 + wc * 128, lane, split);
+  epi(acc, m0 + wr * 128, n0 + wc * 128, lane, split, smem);
 }
 
 template <int DT, int AK, int BKIND, class Epi>
@@ -715,11 +761,12 @@ static inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b)
 // GEMM launchers
 // ---------------------------------------------------------------------------------
 hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
-                           int64_t V, float2 *partials, int64_t ld_part, hipStream_t s) {
+                           int64_t V, float2 *partials, int64_t ld_part, const int *boff,
+                           const unsigned *bent, float *zg, int32_t K, hipStream_t s) {
   Operand A{W, d, (int)V, (int)d, 256};
   Operand B{h_c, d, (int)rows, (int)d, 256};
   GemmGrid G{cdiv(V, kTile), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
-  EpiFwdLse e{partials, ld_part, (int)V, (int)rows};
+  EpiFwdLse e{partials, ld_part, (int)V, (int)rows, boff, bent, G.ntn, zg, (int)K};
   return dtype == 1 ? run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s)
                     : run_gemm<0, OP_KC, OP_KC>(A, B, G, e, s);
 }
@@ -818,62 +865,107 @@ hipError_t launch_validate(const int32_t *idx, const float *p, int64_t NK, int64
   return hipGetLastError();
 }
 
-// One wave per token row; four teacher entries at a time.
-template <int DT>
-__global__ void k_gather(const void *h, const void *W, const int32_t *idx, int rows, int d,
-                         int K, float *zg) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  constexpr int CH = DT == 1 ? 8 : 4;
-  const int nchunks = d / CH;
-  for (int k0 = 0; k0 < K; k0 += 4) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    long long vrow[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) vrow[u] = (k0 + u < K) ? idx[(long long)r * K + k0 + u] : -1;
-    for (int ci = lane; ci < nchunks; ci += 64) {
-      if (DT == 1) {
-        const u32x4 hv = *(const u32x4 *)((const unsigned short *)h + (long long)r * d + ci * CH);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (vrow[u] < 0) continue;
-          const u32x4 wv = *(const u32x4 *)((const unsigned short *)W + vrow[u] * d + ci * CH);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[u] = fmaf(__uint_as_float(hv[e] << 16), __uint_as_float(wv[e] << 16), acc[u]);
-            acc[u] = fmaf(__uint_as_float(hv[e] & 0xFFFF0000u), __uint_as_float(wv[e] & 0xFFFF0000u),
-                          acc[u]);
-          }
-        }
-      } else {
-        const f32x4 hv = *(const f32x4 *)((const float *)h + (long long)r * d + ci * CH);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (vrow[u] < 0) continue;
-          const f32x4 wv = *(const f32x4 *)((const float *)W + vrow[u] * d + ci * CH);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[u] = fmaf(hv[e], wv[e], acc[u]);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float sum = wave_sum(acc[u]);
-      if (lane == 0 && k0 + u < K) zg[(long long)r * K + k0 + u] = sum;
-    }
+// ---------------------------------------------------------------------------------
+// Buckets of teacher hits per output tile of the logits GEMMs (a counting sort).
+// Key of entry (row r, k) of a chunk: (idx >> 8) * ntn + (r >> 8).  A block takes 8 rows,
+// which share one token tile, and aggregates its keys in LDS before touching global
+// counters (the Zipf head puts about half of all hits in the first vocabulary tile).
+// With more than kBucketLdsBins vocabulary tiles the blocks count in global memory.
+// ---------------------------------------------------------------------------------
+constexpr int kBucketLdsBins = 8192;
+
+__global__ void k_bucket_count(const int32_t *idx, int rows, int K, int ntm, int ntn,
+                               int *counts) {
+  extern __shared__ int hist[];
+  const int t = threadIdx.x;
+  const bool lds = ntm <= kBucketLdsBins;
+  const int r0 = blockIdx.x * 8;
+  const int n = min(8, rows - r0) * K;
+  const int32_t *ip = idx + (long long)r0 * K;
+  const int tn = r0 >> 8;
+  if (lds) {
+    for (int i = t; i < ntm; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int e = t; e < n; e += blockDim.x) atomicAdd(&hist[ip[e] >> 8], 1);
+    __syncthreads();
+    for (int i = t; i < ntm; i += blockDim.x)
+      if (hist[i]) atomicAdd(&counts[i * ntn + tn], hist[i]);
+  } else {
+    for (int e = t; e < n; e += blockDim.x) atomicAdd(&counts[(ip[e] >> 8) * ntn + tn], 1);
   }
 }
 
-hipError_t launch_gather(int dtype, const void *h_c, const void *W, const int32_t *idx_c,
-                         int64_t rows, int64_t d, int32_t K, float *zg, hipStream_t s) {
-  const int blocks = cdiv(rows, 4);
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_gather<1>, dim3(blocks), dim3(256), 0, s, h_c, W, idx_c, (int)rows,
-                       (int)d, (int)K, zg);
-  else
-    hipLaunchKernelGGL(k_gather<0>, dim3(blocks), dim3(256), 0, s, h_c, W, idx_c, (int)rows,
-                       (int)d, (int)K, zg);
+// One block of 1024 threads: offsets = exclusive scan of counts; counts and cursors are
+// cleared for the next chunk.
+__global__ void k_bucket_scan(int *counts, int nkeys, int *offsets, int *cursor) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (nkeys + 1023) / 1024;
+  const int b = min(nkeys, t * per), e = min(nkeys, b + per);
+  int s = 0;
+  for (int i = b; i < e; ++i) s += counts[i];
+  part[t] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - s;
+  for (int i = b; i < e; ++i) {
+    offsets[i] = run;
+    run += counts[i];
+    counts[i] = 0;
+    cursor[i] = 0;
+  }
+  if (t == 1023) offsets[nkeys] = part[1023];
+}
+
+__global__ void k_bucket_fill(const int32_t *idx, int rows, int K, int ntm, int ntn,
+                              const int *offsets, int *cursor, unsigned *entries) {
+  extern __shared__ int sh[];
+  const int t = threadIdx.x;
+  const bool lds = ntm <= kBucketLdsBins;
+  int *hist = sh, *base = sh + ntm;
+  const int r0 = blockIdx.x * 8;
+  const int n = min(8, rows - r0) * K;
+  const int32_t *ip = idx + (long long)r0 * K;
+  const int tn = r0 >> 8;
+  if (lds) {
+    for (int i = t; i < ntm; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int e = t; e < n; e += blockDim.x) atomicAdd(&hist[ip[e] >> 8], 1);
+    __syncthreads();
+    for (int i = t; i < ntm; i += blockDim.x)
+      if (hist[i]) {
+        base[i] = offsets[i * ntn + tn] + atomicAdd(&cursor[i * ntn + tn], hist[i]);
+        hist[i] = 0;
+      }
+    __syncthreads();
+  }
+  for (int e = t; e < n; e += blockDim.x) {
+    const int v = ip[e], bin = v >> 8, q = e / K, r = r0 + q, k = e - q * K;
+    const int pos = lds ? base[bin] + atomicAdd(&hist[bin], 1)
+                        : offsets[bin * ntn + tn] + atomicAdd(&cursor[bin * ntn + tn], 1);
+    entries[pos] = (unsigned)(r & 255) | ((unsigned)(v & 255) << 8) | ((unsigned)k << 16);
+  }
+}
+
+hipError_t launch_buckets(const int32_t *idx_c, int64_t rows, int32_t K, int64_t V, int *counts,
+                          int *cursor, int *offsets, unsigned *entries, hipStream_t s) {
+  const int ntm = (int)((V + kTile - 1) / kTile), ntn = (int)((rows + kTile - 1) / kTile);
+  const int blocks = (int)((rows + 7) / 8);
+  const bool lds = ntm <= kBucketLdsBins;
+  hipLaunchKernelGGL(k_bucket_count, dim3(blocks), dim3(256), lds ? ntm * 4 : 0, s, idx_c,
+                     (int)rows, (int)K, ntm, ntn, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, counts, ntm * ntn, offsets, cursor);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bucket_fill, dim3(blocks), dim3(256), lds ? 2 * ntm * 4 : 0, s, idx_c,
+                     (int)rows, (int)K, ntm, ntn, offsets, cursor, entries);
   return hipGetLastError();
 }
 
