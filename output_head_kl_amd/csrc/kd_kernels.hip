@@ -325,13 +325,14 @@ struct EpiFwdLse {
   int ntn;                // token tiles in the chunk
   float *zg;              // [rows][K] logits at the teacher's indices
   int K;
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
+  template <int NCB>
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][NCB], int m0, int n0, int lane,
                                              int, char *smem) const {
     if (m0 < V) {
       const bool full = m0 + 128 <= V;
       const int vl = m0 + (lane >> 5) * 4;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
         float mx = -INFINITY;
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
@@ -360,9 +361,9 @@ struct EpiFwdLse {
     const int key = tm * ntn + tn;
     const int beg = boff[key], end = boff[key + 1];
     if (beg == end) return;
-    const int t = threadIdx.x, w = t >> 6, wr = w >> 1, wc = w & 1;
+    const int t = threadIdx.x, wr = (m0 & 255) >> 7;
     constexpr int P = 68;
-    const int cl0 = wc * 128 + (lane & 31);
+    const int cl0 = (n0 & 255) + (lane & 31);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       __syncthreads();
@@ -371,7 +372,7 @@ struct EpiFwdLse {
         for (int h = 0; h < 2; ++h) {
           const int rb = (q & 1) * 2 + h;
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
+          for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const int vloc = h * 32 + g * 8 + (lane >> 5) * 4;
@@ -382,7 +383,7 @@ struct EpiFwdLse {
         }
       }
       __syncthreads();
-      for (int e = beg + t; e < end; e += 256) {
+      for (int e = beg + t; e < end; e += blockDim.x) {
         const unsigned ent = bent[e];
         const int cl = ent & 255, vloc = (ent >> 8) & 255, k = ent >> 16;
         if ((vloc >> 6) == q)
@@ -400,11 +401,12 @@ struct EpiBwdDz {
   long long ts;  // C_alloc * 256
   const float *lse, *sM;
   int V, rows;
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
+  template <int NCB>
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][NCB], int m0, int n0, int lane,
                                              int, char *) const {
     const int vl = m0 + (lane >> 5) * 4;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       const int c = n0 + cb * 32 + (lane & 31);
       if (c >= rows) continue;
       const float l2 = lse[c] * kLog2e;
@@ -435,12 +437,13 @@ struct EpiDhPart {
   float *part;
   long long split_stride, ld;  // C_alloc*d_pad, d_pad
   int rows;
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
+  template <int NCB>
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][NCB], int m0, int n0, int lane,
                                              int split, char *) const {
     float *base = part + split * split_stride;
     const int jl = m0 + (lane >> 5) * 4;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       const int c = n0 + cb * 32 + (lane & 31);
       if (c >= rows) continue;
 #pragma unroll
@@ -464,11 +467,12 @@ struct EpiDhPart {
 struct EpiDw {
   float *dW;
   int d, V, accumulate;
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int m0, int n0, int lane,
+  template <int NCB>
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][NCB], int m0, int n0, int lane,
                                              int, char *) const {
     const int vl = m0 + (lane >> 5) * 4;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       const int j = n0 + cb * 32 + (lane & 31);
       if (j >= d) continue;
 #pragma unroll
@@ -513,7 +517,7 @@ template <int BK> struct Geo {
   static constexpr int STAGE = 2 * OPB;
   static constexpr int ROWB = BK * 2;        // KC row bytes
   static constexpr int CPR = BK / 8;         // KC 16-B chunks per row
-  static constexpr int NI = BK / 8;          // buffer loads per wave per operand per stage
+  static constexpr int LOADS = BK / 2;       // 1-KB buffer loads per operand per stage
   // KC swizzle: a 16-lane LDS phase reads 16 rows of one logical chunk; rows that share
   // a 256-B bank window (same row % (256/ROWB)) get distinct chunks.
   static __device__ __forceinline__ int kc_swz(int row) {
@@ -521,20 +525,20 @@ template <int BK> struct Geo {
   }
 };
 
-// Per-lane description of the chunks (of 16 B) one lane moves per operand per stage.
-template <int BK> struct LaneChunks {
-  int rel[Geo<BK>::NI];   // byte offset relative to the operand base of the stage
-  int mn[Geo<BK>::NI];    // mn offset of the chunk within the tile
-  int k[Geo<BK>::NI];     // k offset of the chunk within the stage
+// Per-lane description of the NI chunks (of 16 B) one lane moves per operand per stage.
+template <int NI> struct LaneChunks {
+  int rel[NI];   // byte offset relative to the operand base of the stage
+  int mn[NI];    // mn offset of the chunk within the tile
+  int k[NI];     // k offset of the chunk within the stage
 };
 
-template <int KIND, int BK>
-__device__ __forceinline__ LaneChunks<BK> lane_chunks(long long ld, int w, int lane) {
+template <int KIND, int BK, int NI>
+__device__ __forceinline__ LaneChunks<NI> lane_chunks(long long ld, int w, int lane) {
   using GG = Geo<BK>;
-  LaneChunks<BK> c;
+  LaneChunks<NI> c;
 #pragma unroll
-  for (int j = 0; j < GG::NI; ++j) {
-    const int q = (w * GG::NI + j) * 64 + lane;   // chunk position in LDS (16 B units)
+  for (int j = 0; j < NI; ++j) {
+    const int q = (w * NI + j) * 64 + lane;   // chunk position in LDS (16 B units)
     if (KIND == OP_KC) {
       const int row = q / GG::CPR, kc = (q % GG::CPR) ^ GG::kc_swz(row);
       c.mn[j] = row;
@@ -550,19 +554,18 @@ __device__ __forceinline__ LaneChunks<BK> lane_chunks(long long ld, int w, int l
   return c;
 }
 
-template <int KIND, int BK> struct Loader {
-static __device__ __forceinline__ void issue(const Operand &op, const LaneChunks<BK> &c, int mn0,
+template <int KIND, int NI> struct Loader {
+static __device__ __forceinline__ void issue(const Operand &op, const LaneChunks<NI> &c, int mn0,
                                              int k0, char *lds, int w) {
-  using GG = Geo<BK>;
   const unsigned short *base = (const unsigned short *)op.ptr;
   base += op_index(op, KIND, mn0, k0);   // a stage never crosses a 256-column block
   __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
-  for (int j = 0; j < GG::NI; ++j) {
+  for (int j = 0; j < NI; ++j) {
     const bool ok = (mn0 + c.mn[j] < op.mn_ext) && (k0 + c.k[j] < op.k_ext);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (LDS_AS void *)((LDS_AS char *)lds + (w * GG::NI + j) * 1024), 16,
+        rs, (LDS_AS void *)((LDS_AS char *)lds + (w * NI + j) * 1024), 16,
         ok ? c.rel[j] : OOB, 0, 0, 0);
   }
 }
@@ -590,21 +593,12 @@ template <int BK> struct PFrag<OP_MC, BK> {
   }
 };
 
-// s_waitcnt with vmcnt <= n (n a multiple of 8, at most 56) and, with LGKM0, lgkmcnt == 0.
-// Immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
-template <bool LGKM0>
-__device__ __forceinline__ void wait_vm(int n) {
-  constexpr int base = LGKM0 ? 0x0070 : 0x0F70;
-  switch (n >= 56 ? 7 : n / 8) {
-    case 0: __builtin_amdgcn_s_waitcnt(base | 0x0); break;
-    case 1: __builtin_amdgcn_s_waitcnt(base | 0x8); break;
-    case 2: __builtin_amdgcn_s_waitcnt(base | 0x4000); break;
-    case 3: __builtin_amdgcn_s_waitcnt(base | 0x4008); break;
-    case 4: __builtin_amdgcn_s_waitcnt(base | 0x8000); break;
-    case 5: __builtin_amdgcn_s_waitcnt(base | 0x8008); break;
-    case 6: __builtin_amdgcn_s_waitcnt(base | 0xC000); break;
-    default: __builtin_amdgcn_s_waitcnt(base | 0xC008); break;
-  }
+// s_waitcnt with vmcnt <= N and, with LGKM0, lgkmcnt == 0.  Immediate: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 (left at their maxima unless LGKM0).
+template <int N, bool LGKM0>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((LGKM0 ? 0x0070 : 0x0F70) | (N & 15) | ((N >> 4) << 14));
 }
 }  // namespace pipe
 
@@ -618,15 +612,24 @@ __device__ __forceinline__ void wait_vm(int n) {
 #define KD_SG_VMEM 0x020
 #define KD_SG_DSRD 0x100
 
-template <int AK, int BKIND, class Epi, int NST = 5, int BK = 32>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// WN = waves along n: 2 gives 4 waves of 128 x 128 (one per SIMD, 256 accumulators
+// each), 4 gives 8 waves of 128 x 64 (two per SIMD, so one wave's MFMAs cover the
+// other's waits).
+template <int AK, int BKIND, class Epi, int NST = 5, int BK = 32, int WN = 2>
+__global__ __attribute__((amdgpu_flat_work_group_size(128 * WN, 128 * WN),
+                          amdgpu_waves_per_eu(WN / 2, WN / 2)))
 void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
   using namespace pipe;
   using GG = Geo<BK>;
+  constexpr int NW = 2 * WN;            // waves
+  constexpr int NCB = 8 / WN;           // 32-column MFMA blocks per wave
+  constexpr int WNC = 32 * NCB;         // columns per wave
+  constexpr int NI = GG::LOADS / NW;    // buffer loads per wave per operand per stage
   constexpr int S = BK / 16;            // 16-k substeps per stage
-  constexpr int LPS = 2 * GG::NI;       // buffer loads per wave per stage
-  // LDS reads per substep: 4 fragments per operand, 2 transposed reads per MC fragment
-  constexpr int NRD = 4 * (AK == OP_MC ? 2 : 1) + 4 * (BKIND == OP_MC ? 2 : 1);
+  constexpr int LPS = 2 * NI;           // buffer loads per wave per stage
+  constexpr int NMF = 4 * NCB;          // MFMAs per wave per substep
+  // LDS reads per substep: one per fragment, two per transposed (MC) fragment
+  constexpr int NRD = 4 * (AK == OP_MC ? 2 : 1) + NCB * (BKIND == OP_MC ? 2 : 1);
   __shared__ __attribute__((aligned(1024))) char smem[NST * GG::STAGE];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -648,34 +651,34 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wr = w >> 1, wc = w & 1;
-  const LaneChunks<BK> ca = lane_chunks<AK, BK>(A.ld, w, lane);
-  const LaneChunks<BK> cb = lane_chunks<BKIND, BK>(B.ld, w, lane);
+  const int wr = w / WN, wc = w % WN;
+  const LaneChunks<NI> ca = lane_chunks<AK, BK, NI>(A.ld, w, lane);
+  const LaneChunks<NI> cb = lane_chunks<BKIND, BK, NI>(B.ld, w, lane);
   // k beyond this split's range reads zero (and moves no data)
   Operand Ak = A, Bk = B;
   Ak.k_ext = min(A.k_ext, ke);
   Bk.k_ext = min(B.k_ext, ke);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NCB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NCB; ++j) acc[i][j] = f32x16{};
 
   // Prologue: every slot loading (stages past the end are all-zero loads, so the
   // count of loads in flight is the same in every iteration); stage 0 landed.
   for (int s = 0; s < NST; ++s) {
-    Loader<AK, BK>::issue(Ak, ca, m0, kb + s * BK, smem + s * GG::STAGE, w);
-    Loader<BKIND, BK>::issue(Bk, cb, n0, kb + s * BK, smem + s * GG::STAGE + GG::OPB, w);
+    Loader<AK, NI>::issue(Ak, ca, m0, kb + s * BK, smem + s * GG::STAGE, w);
+    Loader<BKIND, NI>::issue(Bk, cb, n0, kb + s * BK, smem + s * GG::STAGE + GG::OPB, w);
   }
-  wait_vm<false>(LPS * (NST - 1));
+  wait_vm<LPS * (NST - 1), false>();
   __syncthreads();
 
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[2][4], fb[2][NCB];
 #pragma unroll
   for (int i = 0; i < 4; ++i) fa[0][i] = PFrag<AK, BK>::load(smem, wr * 128 + i * 32, 0, lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fb[0][j] = PFrag<BKIND, BK>::load(smem + GG::OPB, wc * 128 + j * 32, 0, lane);
+  for (int j = 0; j < NCB; ++j) fb[0][j] = PFrag<BKIND, BK>::load(smem + GG::OPB, wc * WNC + j * 32, 0, lane);
 
   int bcur = 0;  // ring slot of stage it
   for (int it = 0; it < nk; ++it) {
@@ -688,24 +691,24 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
       for (int i = 0; i < 4; ++i)
         fa[(ss + 1) & 1][i] = PFrag<AK, BK>::load(cur, wr * 128 + i * 32, ss + 1, lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[(ss + 1) & 1][j] = PFrag<BKIND, BK>::load(cur + GG::OPB, wc * 128 + j * 32, ss + 1, lane);
+      for (int j = 0; j < NCB; ++j)
+        fb[(ss + 1) & 1][j] = PFrag<BKIND, BK>::load(cur + GG::OPB, wc * WNC + j * 32, ss + 1, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mma(fa[ss & 1][i], fb[ss & 1][j], acc[i][j]);
+        for (int j = 0; j < NCB; ++j) acc[i][j] = mma(fa[ss & 1][i], fb[ss & 1][j], acc[i][j]);
+      // one or two LDS reads in the shadow of each MFMA
 #pragma unroll
-      for (int q = 0; q < NRD; ++q) {
+      for (int q = 0; q < NMF; ++q) {
         __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(KD_SG_DSRD, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(KD_SG_DSRD, (NRD + NMF - 1) / NMF, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 16 - NRD < 0 ? 0 : 16 - NRD, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
 
     // Stage it+1 must have landed for every wave, and every wave must hold the whole of
     // stage it in registers or accumulators, since its slot is refilled next.
-    wait_vm<true>(LPS * (NST - 2));
+    wait_vm<LPS * (NST - 2), true>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -715,30 +718,32 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[0][i] = PFrag<AK, BK>::load(nx, wr * 128 + i * 32, 0, lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[0][j] = PFrag<BKIND, BK>::load(nx + GG::OPB, wc * 128 + j * 32, 0, lane);
-    Loader<AK, BK>::issue(Ak, ca, m0, kb + (it + NST) * BK, cur, w);
-    Loader<BKIND, BK>::issue(Bk, cb, n0, kb + (it + NST) * BK, cur + GG::OPB, w);
+    for (int j = 0; j < NCB; ++j) fb[0][j] = PFrag<BKIND, BK>::load(nx + GG::OPB, wc * WNC + j * 32, 0, lane);
+    Loader<AK, NI>::issue(Ak, ca, m0, kb + (it + NST) * BK, cur, w);
+    Loader<BKIND, NI>::issue(Bk, cb, n0, kb + (it + NST) * BK, cur + GG::OPB, w);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma(fa[(S - 1) & 1][i], fb[(S - 1) & 1][j], acc[i][j]);
-    // reads for the next stage first (they gate the next iteration), loads after
+      for (int j = 0; j < NCB; ++j)
+        acc[i][j] = mma(fa[(S - 1) & 1][i], fb[(S - 1) & 1][j], acc[i][j]);
+    // reads for the next stage in the first half of the MFMAs (they gate the next
+    // iteration), loads in the second half
 #pragma unroll
-    for (int q = 0; q < (NRD < 8 ? NRD : 8); ++q) {
+    for (int q = 0; q < NMF / 2; ++q) {
       __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(KD_SG_DSRD, NRD > 8 ? 2 : 1, 1);
+      __builtin_amdgcn_sched_group_barrier(KD_SG_DSRD, (2 * NRD + NMF - 1) / NMF, 1);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NMF / 2; ++q) {
       __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM, LPS / 8, 1);
+      __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM, (2 * LPS + NMF - 1) / NMF, 1);
       __builtin_amdgcn_sched_group_barrier(KD_SG_VALU, 2, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     bcur = bnext;
   }
-  wait_vm<false>(0);  // the zero loads issued past the end
-  epi(acc, m0 + wr * 128, n0 + wc * 128, lane, split, smem);
+  wait_vm<0, false>();  // the zero loads issued past the end
+  epi(acc, m0 + wr * 128, n0 + wc * WNC, lane, split, smem);
 }
 
 template <int DT, int AK, int BKIND, class Epi>
@@ -746,9 +751,9 @@ static hipError_t run_gemm(const Operand &A, const Operand &B, const GemmGrid &G
                            hipStream_t s) {
   const long long T = (long long)G.ntm * G.ntn * G.nsplit;
   if (T <= 0) return hipSuccess;
-  if (DT == 1)
-    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKIND, Epi>), dim3((unsigned)T), dim3(256), 0, s, A,
-                       B, G, epi);
+  if (DT == 1)  // 8 waves (two per SIMD), a ring of 4 stages of 32 k
+    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKIND, Epi, 4, 32, 4>), dim3((unsigned)T), dim3(512),
+                       0, s, A, B, G, epi);
   else
     hipLaunchKernelGGL((gemm_kernel<DT, AK, BKIND, Epi>), dim3((unsigned)T), dim3(256), 0, s, A,
                        B, G, epi);
