@@ -37,6 +37,10 @@ def parse():
                     help="token rows of the workload timed through the CPU oracle")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip per-kernel HIP-event timing inside the timed region")
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="measure peak device memory of one call for N = 4K .. 256K tokens "
+                         "(d=3072, V=128256, K=100, chunk 4096) and fit a + b*N; prints one "
+                         "JSON line and exits")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="after the run, launch one plain device copy of this many GiB "
                          "(a kernel of known traffic, for scaling HBM byte counters)")
@@ -83,8 +87,69 @@ def cpu_baseline(inp, rows):
                       f"float64 numpy, loss + dh + dW, {dt:.1f} s"}
 
 
+def memory_sweep():
+    """Peak device memory of one fused call (inputs, outputs, workspace) against N.
+
+    Inputs are generated directly in their storage types, so the peak holds only h, W,
+    idx, p, mask, the outputs and the workspace.  The device's free-memory drop across
+    the call is compared with the growth of torch's reserved pool: equal values show
+    the library allocated nothing of its own."""
+    import torch
+
+    import output_head_kl_amd as kd
+    d, V, K, chunk = 3072, 128256, 100, 4096
+    g = torch.Generator(device="cuda").manual_seed(20260804)
+    Ns = [4096, 8192, 16384, 32768, 65536, 131072, 262144]
+    W = torch.randn(V, d, device="cuda", generator=g, dtype=torch.bfloat16) * (2.0 / d ** 0.5)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    peaks, rows = [], []
+    for N in Ns:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        h = torch.randn(N, d, device="cuda", generator=g, dtype=torch.bfloat16)
+        idx = torch.randint(0, V, (N, K), device="cuda", generator=g, dtype=torch.int32)
+        p = torch.rand(N, K, device="cuda", generator=g)
+        p.mul_(1.0 / K)
+        mask = torch.ones(N, dtype=torch.uint8, device="cuda")
+        ws_bytes = kd.workspace_bytes(N, d, V, K, chunk)
+        torch.cuda.synchronize()
+        free0, _ = torch.cuda.mem_get_info()
+        res0 = torch.cuda.memory_reserved()
+        out = kd.fwd_bwd(h, W, idx, p, mask, chunk=chunk)
+        torch.cuda.synchronize()
+        free1, _ = torch.cuda.mem_get_info()
+        res1 = torch.cuda.memory_reserved()
+        peaks.append(torch.cuda.max_memory_allocated())
+        largest = max(ws_bytes, N * d * 2, V * d * 4)   # workspace, dh, dW
+        rows.append({"N": N, "peak_bytes": peaks[-1], "workspace_bytes": ws_bytes,
+                     "device_free_drop_bytes": free0 - free1,
+                     "torch_reserved_growth_bytes": res1 - res0,
+                     "largest_allocation_bytes": largest,
+                     "dense_bf16_logits_bytes": N * V * 2})
+        del h, idx, p, mask, out
+        print(f"[memory] N={N}: peak {peaks[-1] / 2**30:.3f} GiB, free drop "
+              f"{(free0 - free1) / 2**20:.1f} MiB, reserved growth {(res1 - res0) / 2**20:.1f} MiB",
+              file=sys.stderr, flush=True)
+    x = np.array(Ns, dtype=np.float64)
+    y = np.array(peaks, dtype=np.float64)
+    b, a = np.polyfit(x, y, 1)
+    fit = a + b * x
+    r2 = 1.0 - np.sum((y - fit) ** 2) / np.sum((y - y.mean()) ** 2)
+    res = {"memory_sweep": {"d": d, "V": V, "K": K, "chunk": chunk, "dtype": "bf16",
+                            "W_bytes": V * d * 2, "allocated_before_sweep_bytes": base,
+                            "fit_intercept_bytes": a, "fit_bytes_per_token": b, "r2": r2,
+                            "max_abs_residual_bytes": float(np.abs(y - fit).max()),
+                            "points": rows}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
+    if args.memory_sweep:
+        memory_sweep()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
               "multi-GPU path; see DESIGN.md for how the work would shard.", file=sys.stderr)
