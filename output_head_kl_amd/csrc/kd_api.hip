@@ -41,7 +41,7 @@ std::mutex g_prof_mu;
 
 const char *const kClassNames[kd::KC_COUNT] = {
     "validate", "fwd_gemm_lse", "bucket", "combine_lse_loss", "bwd_gemm_dz",
-    "scatter",  "dh_gemm",      "dh_reduce", "dw_gemm",      "misc"};
+    "scatter",  "dh_gemm",      "dh_reduce", "dw_gemm",      "w_transpose", "misc"};
 
 #define HIPCHK(expr)                                                                 \
   do {                                                                               \
@@ -134,6 +134,7 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->off_bcursor = take((size_t)L->nkeys * 4);
   L->off_boff = take((size_t)(L->nkeys + 1) * 4);
   L->off_bent = take((size_t)L->C_alloc * K * 4);
+  L->off_wt = take(dtype == KD_BF16 ? (size_t)L->V_pad * d * 2 : 0);
   L->total = off;
   return true;
 }
@@ -230,6 +231,9 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
   }
   const float inv_count = count > 0 ? (float)(1.0 / (double)count) : 0.f;
   LAUNCH(kd::KC_MISC, kd::launch_fill_zero(bcount, (size_t)L.nkeys * 4, stream));
+  void *WT = ws + L.off_wt;
+  if (count > 0 && dtype == KD_BF16)
+    LAUNCH(kd::KC_TRANSPOSE, kd::launch_transpose_w(W, V, d, L.V_pad, WT, stream));
 
   int chunk_i = 0;
   for (int64_t c0 = 0; c0 < N; c0 += L.C, ++chunk_i) {
@@ -255,7 +259,7 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
                                stream));
     LAUNCH(kd::KC_SCATTER,
            kd::launch_scatter(dtype, dz, L.C_alloc, idx_c, p_c, srow, rows, K, stream));
-    LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, rows, d, V, L.V_pad, L.nsplit,
+    LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, WT, rows, d, V, L.V_pad, L.nsplit,
                                               L.k_split, dhpart, L.d_pad, L.C_alloc, stream));
     LAUNCH(kd::KC_DH_REDUCE, kd::launch_dh_reduce(dtype, dhpart, L.nsplit, L.C_alloc, L.d_pad,
                                                   rows, d, (char *)dh + c0 * d * es, stream));

@@ -24,6 +24,7 @@ enum KClass {
   KC_DH_GEMM,      // dh partials (split over the vocabulary)
   KC_DH_REDUCE,    // dh partials summed and rounded
   KC_DW_GEMM,      // dW accumulation
+  KC_TRANSPOSE,    // W copied to vocabulary-contiguous blocks for the dh GEMM
   KC_MISC,         // fills, loss accumulation and finalisation
   KC_COUNT
 };
@@ -39,7 +40,7 @@ struct Layout {
   int64_t k_split;    // vocabulary rows per split (a multiple of 256)
   int64_t nkeys;      // buckets per chunk: ceil(V / 256) * C_alloc / 256
   size_t off_flags, off_acc, off_partials, off_lse, off_sM, off_s, off_rowterm, off_zg,
-      off_dz, off_dhpart, off_bcount, off_bcursor, off_boff, off_bent, total;
+      off_dz, off_dhpart, off_bcount, off_bcursor, off_boff, off_bent, off_wt, total;
 };
 
 bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
@@ -75,8 +76,13 @@ hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
 hipError_t launch_scatter(int dtype, void *dz, int64_t C_alloc, const int32_t *idx_c,
                           const float *p_c, const float *srow, int64_t rows, int32_t K,
                           hipStream_t s);
-hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, int64_t rows, int64_t d,
-                          int64_t V, int64_t V_pad, int nsplit, int64_t k_split,
+// W^T in blocks of 256 vocabulary entries (bf16 only): element (v, j) of W at
+// WT[(v / 256) * d * 256 + j * 256 + v % 256], zero for V <= v < V_pad.
+hipError_t launch_transpose_w(const void *W, int64_t V, int64_t d, int64_t V_pad, void *WT,
+                              hipStream_t s);
+// dh partials; bf16 reads W through WT (above), fp32 reads W itself.
+hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, const void *WT, int64_t rows,
+                          int64_t d, int64_t V, int64_t V_pad, int nsplit, int64_t k_split,
                           float *part, int64_t d_pad, int64_t C_alloc, hipStream_t s);
 hipError_t launch_dh_reduce(int dtype, const float *part, int nsplit, int64_t C_alloc,
                             int64_t d_pad, int64_t rows, int64_t d, void *dh, hipStream_t s);

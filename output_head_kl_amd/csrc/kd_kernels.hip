@@ -790,16 +790,58 @@ hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
   return run_gemm<0, OP_KC, OP_KC>(A, B, G, e, s);
 }
 
-hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, int64_t rows, int64_t d,
-                          int64_t V, int64_t V_pad, int nsplit, int64_t k_split, float *part,
-                          int64_t d_pad, int64_t C_alloc, hipStream_t s) {
-  // D[j][c] = sum_v W[v][j] dz[c][v]: A = W as MC ([v][j]), B = dz as KC ([c][v]).
-  Operand A{W, d, (int)d, (int)V, 256};
+hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, const void *WT, int64_t rows,
+                          int64_t d, int64_t V, int64_t V_pad, int nsplit, int64_t k_split,
+                          float *part, int64_t d_pad, int64_t C_alloc, hipStream_t s) {
+  // D[j][c] = sum_v W[v][j] dz[c][v]; B = dz as KC ([c][v] in 256-column blocks).
   Operand B{dz, 256, (int)rows, (int)V_pad, C_alloc * 256};
   GemmGrid G{cdiv(d, kTile), cdiv(rows, kTile), nsplit, (int)k_split, (int)V_pad, 0};
   EpiDhPart e{part, C_alloc * d_pad, d_pad, (int)rows};
-  return dtype == 1 ? run_gemm<1, OP_MC, OP_KC>(A, B, G, e, s)
-                    : run_gemm<0, OP_MC, OP_KC>(A, B, G, e, s);
+  if (dtype == 1) {
+    // A = W^T as KC: [j][v] in blocks of 256 v, zero-padded to V_pad, so both operands
+    // are read with plain 16-byte LDS reads
+    Operand A{WT, 256, (int)d, (int)V_pad, d * 256};
+    return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
+  }
+  Operand A{W, d, (int)d, (int)V, 256};  // A = W as MC ([v][j])
+  return run_gemm<0, OP_MC, OP_KC>(A, B, G, e, s);
+}
+
+// W [V][d] bf16 -> WT blocks: element (v, j) at (v / 256) * d * 256 + j * 256 + v % 256,
+// zero for V <= v < V_pad.  A block moves a 64 (v) x 64 (j) tile through LDS so that
+// both the reads of W rows and the writes of WT rows are 128-byte segments.
+__global__ __launch_bounds__(256) void k_transpose_w(const unsigned short *W, int V, int d,
+                                                     int V_pad, unsigned short *WT) {
+  __shared__ __attribute__((aligned(16))) unsigned short t[64][72];
+  const int v0 = blockIdx.x * 64, j0 = blockIdx.y * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int q = tid; q < 512; q += 256) {
+    const int r = q >> 3, c8 = (q & 7) * 8;
+    const int v = v0 + r, j = j0 + c8;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (v < V && j < d) val = *(const u32x4 *)(W + (long long)v * d + j);  // d % 8 == 0
+    *(u32x4 *)&t[r][c8] = val;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = tid; q < 512; q += 256) {
+    const int jr = q >> 3, v8 = (q & 7) * 8;
+    const int j = j0 + jr, v = v0 + v8;
+    if (j >= d || v >= V_pad) continue;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (unsigned)t[v8 + 2 * e][jr] | ((unsigned)t[v8 + 2 * e + 1][jr] << 16);
+    *(u32x4 *)(WT + (long long)(v >> 8) * d * 256 + (long long)j * 256 + (v & 255)) = o;
+  }
+}
+
+hipError_t launch_transpose_w(const void *W, int64_t V, int64_t d, int64_t V_pad, void *WT,
+                              hipStream_t s) {
+  const dim3 grid((unsigned)(V_pad / 64), (unsigned)((d + 63) / 64));
+  hipLaunchKernelGGL(k_transpose_w, grid, dim3(256), 0, s, (const unsigned short *)W, (int)V,
+                     (int)d, (int)V_pad, (unsigned short *)WT);
+  return hipGetLastError();
 }
 
 hipError_t launch_dw_gemm(int dtype, const void *dz, const void *h_c, int64_t rows, int64_t d,
