@@ -1016,25 +1016,28 @@ hipError_t launch_buckets(const int32_t *idx_c, int64_t rows, int32_t K, int64_t
   return hipGetLastError();
 }
 
-// 64 token rows per block; wave w folds partials t = w, w+4, ...; lane = row.
-__global__ void k_combine(const float2 *part, int n_lse, long long ld, const float *zg,
-                          const float *p, const uint8_t *mask, int rows, int K, float inv_count,
-                          float *lse_out, float *sM_out, float *s_out, double *rowterm,
-                          float *row_loss, float *row_lse) {
+// 64 token rows per block of 16 waves; lane = row.  Wave w folds the (max, sum-exp)
+// partials t = w, w+16, ... (eight loads in flight per lane) and the teacher entries
+// k = w, w+16, ...; wave 0 then folds the 16 results in a fixed order.
+constexpr int kCombWaves = 16;
+__global__ __launch_bounds__(64 * kCombWaves) void k_combine(
+    const float2 *part, int n_lse, long long ld, const float *zg, const float *p,
+    const uint8_t *mask, int rows, int K, float inv_count, float *lse_out, float *sM_out,
+    float *s_out, double *rowterm, float *row_loss, float *row_lse) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = blockIdx.x * 64 + lane;
   const bool live = r < rows;
   float m = -INFINITY, sum = 0.f;
   if (live) {
-    for (int t0 = w; t0 < n_lse; t0 += 16) {
-      float2 q[4];
+    for (int t0 = w; t0 < n_lse; t0 += 8 * kCombWaves) {
+      float2 q[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = t0 + 4 * u;
+      for (int u = 0; u < 8; ++u) {
+        const int t = t0 + kCombWaves * u;
         q[u] = t < n_lse ? part[(long long)t * ld + r] : make_float2(-INFINITY, 0.f);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         if (q[u].y == 0.f) continue;
         if (q[u].x > m) {
           sum = sum * fast_exp2((m - q[u].x) * kLog2e) + q[u].y;
@@ -1045,14 +1048,13 @@ __global__ void k_combine(const float2 *part, int n_lse, long long ld, const flo
       }
     }
   }
-  __shared__ float sm[4][64], ss[4][64];
-  __shared__ double sd[3][4][64];
+  __shared__ float sm[kCombWaves][64], ss[kCombWaves][64];
+  __shared__ double sd[3][kCombWaves][64];
   sm[w][lane] = m;
   ss[w][lane] = sum;
-  // teacher terms: wave w takes k = w, w+4, ...
   double H = 0.0, PZ = 0.0, Ms = 0.0;
   if (live) {
-    for (int k = w; k < K; k += 4) {
+    for (int k = w; k < K; k += kCombWaves) {
       const double q = p[(long long)r * K + k];
       Ms += q;
       PZ += q * (double)zg[(long long)r * K + k];
@@ -1065,13 +1067,13 @@ __global__ void k_combine(const float2 *part, int n_lse, long long ld, const flo
   __syncthreads();
   if (w == 0 && live) {
     float M = sm[0][lane];
-    for (int i = 1; i < 4; ++i) M = fmaxf(M, sm[i][lane]);
+    for (int i = 1; i < kCombWaves; ++i) M = fmaxf(M, sm[i][lane]);
     float S = 0.f;
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kCombWaves; ++i)
       if (ss[i][lane] != 0.f) S += ss[i][lane] * fast_exp2((sm[i][lane] - M) * kLog2e);
     const float lse = M + logf(S);
     double h = 0.0, pz = 0.0, ms = 0.0;
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kCombWaves; ++i) {
       h += sd[0][i][lane];
       pz += sd[1][i][lane];
       ms += sd[2][i][lane];
@@ -1092,7 +1094,8 @@ hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part
                           int64_t rows, int32_t K, float inv_count, float *lse, float *sM,
                           float *srow, double *rowterm, float *row_loss, float *row_lse,
                           hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(cdiv(rows, 64)), dim3(256), 0, s, partials, (int)n_lse,
+  hipLaunchKernelGGL(k_combine, dim3(cdiv(rows, 64)), dim3(64 * kCombWaves), 0, s, partials,
+                     (int)n_lse,
                      (long long)ld_part, zg, p_c, mask_c, (int)rows, (int)K, inv_count, lse, sM,
                      srow, rowterm, row_loss, row_lse);
   return hipGetLastError();
@@ -1127,38 +1130,56 @@ hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStr
 }
 
 // dz[r][idx[r][k]] -= s[r] * (sum of p over the row's entries with that index).
-// The first entry of each distinct index does the update, so no two threads touch
-// the same element.
+// One wave per row.  Lane k compares its index with every entry of the row (64 at a
+// time through shuffles): the first entry of each distinct index sums the
+// probabilities of its later duplicates in order and does the update, so no two
+// threads touch the same element.
 template <int DT>
-__global__ void k_scatter(void *dz, long long ts, const int32_t *idx, const float *p,
-                          const float *srow, int rows, int K) {
-  const long long g = blockIdx.x * (long long)blockDim.x + threadIdx.x;
-  if (g >= (long long)rows * K) return;
-  const int r = (int)(g / K), k = (int)(g - (long long)r * K);
+__global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, const int32_t *idx,
+                                                 const float *p, const float *srow, int rows,
+                                                 int K) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= rows) return;
   const float sr = srow[r];
   if (sr == 0.f) return;
   const int32_t *ir = idx + (long long)r * K;
   const float *pr = p + (long long)r * K;
-  const int v = ir[k];
-  for (int j = 0; j < k; ++j)
-    if (ir[j] == v) return;
-  float tot = pr[k];
-  for (int j = k + 1; j < K; ++j)
-    if (ir[j] == v) tot += pr[j];
-  if (DT == 1) {
-    unsigned short *q = (unsigned short *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
-    *q = f32_to_bf16(bf16_to_f32(*q) - sr * tot);
-  } else {
-    float *q = (float *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
-    *q = *q - sr * tot;
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int k = k0 + lane;
+    const bool has = k < K;
+    const int v = has ? ir[k] : -1;
+    float tot = has ? pr[k] : 0.f;
+    bool first = has;
+    for (int j0 = 0; j0 < K; j0 += 64) {
+      const int jl = j0 + lane;
+      const int vjl = jl < K ? ir[jl] : -1;
+      const float pjl = jl < K ? pr[jl] : 0.f;
+      const int n = min(64, K - j0);
+      for (int t = 0; t < n; ++t) {
+        const int vj = __shfl(vjl, t, 64);
+        const float pj = __shfl(pjl, t, 64);
+        const int j = j0 + t;
+        if (vj == v) {
+          if (j < k) first = false;
+          else if (j > k) tot += pj;
+        }
+      }
+    }
+    if (!first) continue;
+    if (DT == 1) {
+      unsigned short *q = (unsigned short *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
+      *q = f32_to_bf16(bf16_to_f32(*q) - sr * tot);
+    } else {
+      float *q = (float *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
+      *q = *q - sr * tot;
+    }
   }
 }
 
 hipError_t launch_scatter(int dtype, void *dz, int64_t C_alloc, const int32_t *idx_c,
                           const float *p_c, const float *srow, int64_t rows, int32_t K,
                           hipStream_t s) {
-  const long long n = rows * (long long)K;
-  const int blocks = (int)((n + 255) / 256);
+  const int blocks = (int)((rows + 3) / 4);
   if (dtype == 1)
     hipLaunchKernelGGL(k_scatter<1>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256, idx_c,
                        p_c, srow, (int)rows, (int)K);
