@@ -470,22 +470,40 @@ struct EpiDw {
   template <int NCB>
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][NCB], int m0, int n0, int lane,
                                              int, char *) const {
-    const int vl = m0 + (lane >> 5) * 4;
+    // One buffer resource per wave, from its first row to the end of dW: elements of
+    // rows v >= V lie outside its range and the hardware drops them; lanes with
+    // j >= d get an offset outside every range.  Offsets stay below 128 * d * 4 bytes.
+    const long long rem = (long long)(V - m0) * d * 4;
+    if (rem <= 0) return;
+    const int nrec = rem > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)rem;
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(dW + (long long)m0 * d), (short)0, nrec, 0x00020000);
+    int vo[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int j = n0 + cb * 32 + (lane & 31);
-      if (j >= d) continue;
+      vo[cb] = j < d ? (((lane >> 5) * 4 * d + j) * 4) : (int)0x80000000;
+    }
+    if (accumulate) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
-          if (v >= V) continue;
-          float *p = dW + (long long)v * d + j;
-          if (accumulate)
-            unsafeAtomicAdd(p, acc[rb][cb][i]);
-          else
-            *p = acc[rb][cb][i];
+          const int roff = (rb * 32 + (i >> 2) * 8 + (i & 3)) * d * 4;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[rb][cb][i], rs, vo[cb] + roff, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int roff = (rb * 32 + (i >> 2) * 8 + (i & 3)) * d * 4;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rb][cb][i]), rs,
+                                                  vo[cb] + roff, 0, 0);
         }
     }
   }
@@ -751,8 +769,10 @@ static hipError_t run_gemm(const Operand &A, const Operand &B, const GemmGrid &G
                            hipStream_t s) {
   const long long T = (long long)G.ntm * G.ntn * G.nsplit;
   if (T <= 0) return hipSuccess;
-  if (DT == 1)  // 8 waves (two per SIMD), a ring of 4 stages of 32 k
-    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKIND, Epi, 4, 32, 4>), dim3((unsigned)T), dim3(512),
+  // 8 waves (two per SIMD), two LDS stages of 64 k: a KC operand row is then one
+  // 128-byte segment per stage, which halves the memory requests of k-contiguous operands
+  if constexpr (DT == 1)
+    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKIND, Epi, 2, 64, 4>), dim3((unsigned)T), dim3(512),
                        0, s, A, B, G, epi);
   else
     hipLaunchKernelGGL((gemm_kernel<DT, AK, BKIND, Epi>), dim3((unsigned)T), dim3(256), 0, s, A,
