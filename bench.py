@@ -37,6 +37,10 @@ def parse():
                     help="token rows of the workload timed through the CPU oracle")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip per-kernel HIP-event timing inside the timed region")
+    ap.add_argument("--split", action="store_true",
+                    help="time the forward half (kd_chunked_kl_fwd) and the backward half "
+                         "(kd_chunked_kl_bwd) separately instead of the fused call; prints one "
+                         "JSON line")
     ap.add_argument("--memory-sweep", action="store_true",
                     help="measure peak device memory of one call for N = 4K .. 256K tokens "
                          "(d=3072, V=128256, K=100, chunk 4096) and fit a + b*N; prints one "
@@ -145,6 +149,66 @@ def memory_sweep():
     print(json.dumps(res), flush=True)
 
 
+def _kernel_table(ktimes, steps):
+    out = {}
+    for name, (tot, n) in ktimes.items():
+        if n:
+            out[name] = {"total_ms_per_step": tot / steps, "launches_per_step": n / steps,
+                         "avg_ms": tot / n}
+    return out
+
+
+def bench_split(args, kd, torch, cfg, h, W, idx, p, mask, ws):
+    """Forward half and backward half timed separately (each over args.steps calls)."""
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    loss, row_lse = kd.fwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws)
+    for _ in range(args.warmup):
+        kd.fwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws)
+        kd.bwd(h, W, idx, p, row_lse, g, mask, chunk=cfg.chunk, workspace=ws)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    res_half = {}
+    for half in ("fwd", "bwd"):
+        kd.profile_read()
+        kd.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            if half == "fwd":
+                kd.fwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws)
+            else:
+                kd.bwd(h, W, idx, p, row_lse, g, mask, chunk=cfg.chunk, workspace=ws)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        kd.profile_enable(False)
+        res_half[half] = (el / args.steps * 1e3, _kernel_table(kd.profile_read(), args.steps))
+    fwd_ms, fk = res_half["fwd"]
+    bwd_ms, bk = res_half["bwd"]
+    ms = fwd_ms + bwd_ms
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    gem = {k: v for k, v in bk.items() if k in GEMM_CLASSES}
+    dom = max(gem, key=lambda k: gem[k]["total_ms_per_step"])
+    achieved = 2.0 * cfg.N * cfg.V * cfg.d / gem[dom]["launches_per_step"] / (gem[dom]["avg_ms"] * 1e-3) / 1e12
+    workload = f"fused_kl_split_fwd_bwd_N{cfg.N}_d{cfg.d}_V{cfg.V}_K{cfg.K}_chunk{cfg.chunk}_{cfg.dtype}"
+    res = {
+        "metric": "tokens/s, fused KL as separate forward (kd_chunked_kl_fwd) and backward "
+                  "(kd_chunked_kl_bwd) calls, N=32K d=3072 V=128256 K=100",
+        "value": round(cfg.N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload, "N": cfg.N, "d": cfg.d, "V": cfg.V, "K": cfg.K,
+                   "chunk": cfg.chunk, "mask": cfg.mask},
+        "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+        "fwd_tflops_2NVd": round(2.0 * cfg.N * cfg.V * cfg.d / (fwd_ms * 1e-3) / 1e12, 1),
+        "bwd_tflops_6NVd": round(6.0 * cfg.N * cfg.V * cfg.d / (bwd_ms * 1e-3) / 1e12, 1),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+        "kernels_fwd": fk, "kernels_bwd": bk, "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.memory_sweep:
@@ -182,6 +246,9 @@ def main():
 
     def step():
         return kd.fwd_bwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws)
+
+    if args.split:
+        return bench_split(args, kd, torch, cfg, h, W, idx, p, mask, ws)
 
     for _ in range(args.warmup):
         out = step()

@@ -105,6 +105,50 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype,
                           float *row_loss, float *row_lse, float *zg,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kd_chunked_kl_fwd -- the forward half: loss and the per-token logsumexp.
+ *
+ * The loss as a function of the hidden states with the logits recomputed in the
+ * backward pass (thorstenmeyerai.com article, infographic "Recompute backward";
+ * aimodeling.com article, "Second cut").  Computes exactly the loss, row_loss and zg
+ * of kd_chunked_kl_fwd_bwd (bit for bit, on the same inputs and chunk) and writes
+ *   row_lse   [N]     float32   lse[n] = log sum_v exp z[n,v]   (required when N > 0)
+ * which is the state kd_chunked_kl_bwd reads.  row_loss and zg are optional (NULL =
+ * skip).  dh and dW are not computed.  Same sizes, workspace (kd_workspace_bytes),
+ * stream behaviour and errors as kd_chunked_kl_fwd_bwd; N == 0 writes loss = 0.
+ */
+int kd_chunked_kl_fwd(const void *h, const void *W, int32_t dtype,
+                      const int32_t *topk_idx, const float *topk_p,
+                      const uint8_t *loss_mask,
+                      int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                      float *loss, float *row_lse, float *row_loss, float *zg,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kd_chunked_kl_bwd -- the backward half: dh and dW for an upstream gradient.
+ *
+ * Recomputes the logits chunk by chunk from h and W and forms the closed-form
+ * gradient of the legiblepapers.com summary (Cross-Examination & FAQs, Q5), scaled by
+ * the upstream gradient g = grad_loss[0] of the mean loss:
+ *   dz[n,v] = g * (mask[n]/count) * (M[n]*exp(z[n,v] - row_lse[n]) - sum_{k: idx[n,k]=v} p[n,k])
+ *   dh = dz @ W  (rounded once to dtype),  dW = dz^T @ h  (float32, overwritten).
+ * Inputs as for kd_chunked_kl_fwd_bwd, plus
+ *   row_lse   [N]  float32  device   the logsumexp written by kd_chunked_kl_fwd for the
+ *                                    same h, W and chunk (required when N > 0)
+ *   grad_loss [1]  float32  device   g, read on the device (no host synchronisation)
+ * With g = 1 and row_lse from kd_chunked_kl_fwd, dh and dW equal those of
+ * kd_chunked_kl_fwd_bwd bit for bit.  Teacher entries are validated again (one stream
+ * synchronisation); count == 0 or N == 0 gives dh = 0 and dW = 0.  Same workspace
+ * (kd_workspace_bytes), stream behaviour and errors as kd_chunked_kl_fwd_bwd.
+ */
+int kd_chunked_kl_bwd(const void *h, const void *W, int32_t dtype,
+                      const int32_t *topk_idx, const float *topk_p,
+                      const uint8_t *loss_mask,
+                      int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                      const float *row_lse, const float *grad_loss,
+                      void *dh, float *dW,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Text describing the last non-OK return on the calling thread ("" if none). */
 const char *kd_last_error(void);
 

@@ -12,8 +12,9 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["KDError", "library_path", "workspace_bytes", "fwd_bwd", "profile_enable",
-           "profile_read", "profile_classes", "KD_F32", "KD_BF16"]
+__all__ = ["KDError", "library_path", "workspace_bytes", "fwd_bwd", "fwd", "bwd",
+           "chunked_kl_loss", "profile_enable", "profile_read", "profile_classes", "KD_F32",
+           "KD_BF16"]
 
 KD_F32, KD_BF16 = 0, 1
 _STATUS = {0: "KD_OK", 1: "KD_E_ARG", 2: "KD_E_INDEX", 3: "KD_E_WORKSPACE",
@@ -47,6 +48,12 @@ def _lib():
     lib.kd_chunked_kl_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
                                           vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_fwd_bwd.restype = ctypes.c_int
+    lib.kd_chunked_kl_fwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
+                                      vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_chunked_kl_fwd.restype = ctypes.c_int
+    lib.kd_chunked_kl_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
+                                      vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_chunked_kl_bwd.restype = ctypes.c_int
     lib.kd_last_error.argtypes = []
     lib.kd_last_error.restype = ctypes.c_char_p
     lib.kd_version.restype = ctypes.c_int
@@ -84,19 +91,8 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: bool = False,
-            workspace=None, stream=None):
-    """Mean top-K KL loss with its gradients, computed chunk by chunk on the GPU.
-
-    Args (torch CUDA tensors, contiguous):
-      h [N, d] and W [V, d]: bfloat16 or float32 (same dtype);
-      topk_idx [N, K] int32; topk_p [N, K] float32; loss_mask [N] uint8/bool or None.
-      chunk: token rows whose logits are live at once.
-      rows: also return per-row loss, logsumexp and the logits at the teacher's indices.
-      workspace: optional uint8 tensor of at least ``workspace_bytes(...)`` bytes.
-    Returns (loss[1] f32, dh [N, d] dtype, dW [V, d] f32) and, with ``rows``,
-    (row_loss [N], row_lse [N], zg [N, K]) as float32.
-    """
+def _prep(h, W, topk_idx, topk_p, loss_mask):
+    """Checks dtypes, shapes and contiguity; returns (dtype code, N, d, V, K, mask)."""
     import torch
     dt = _dtype_code(h)
     if W.dtype != h.dtype:
@@ -117,10 +113,39 @@ def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: boo
             loss_mask = loss_mask.view(torch.uint8)
         if loss_mask.dtype != torch.uint8 or tuple(loss_mask.shape) != (N,):
             raise ValueError("loss_mask must be uint8/bool of shape [N]")
-    dev = h.device
-    need = workspace_bytes(N, d, V, K, chunk, dt)
+    return dt, N, d, V, K, loss_mask
+
+
+def _workspace(workspace, N, d, V, K, chunk, dt, dev):
+    import torch
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(workspace_bytes(N, d, V, K, chunk, dt), 256),
+                                dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def _stream(stream, dev):
+    import torch
+    return torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+
+
+def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: bool = False,
+            workspace=None, stream=None):
+    """Mean top-K KL loss with its gradients, computed chunk by chunk on the GPU.
+
+    Args (torch CUDA tensors, contiguous):
+      h [N, d] and W [V, d]: bfloat16 or float32 (same dtype);
+      topk_idx [N, K] int32; topk_p [N, K] float32; loss_mask [N] uint8/bool or None.
+      chunk: token rows whose logits are live at once.
+      rows: also return per-row loss, logsumexp and the logits at the teacher's indices.
+      workspace: optional uint8 tensor of at least ``workspace_bytes(...)`` bytes.
+    Returns (loss[1] f32, dh [N, d] dtype, dW [V, d] f32) and, with ``rows``,
+    (row_loss [N], row_lse [N], zg [N, K]) as float32.
+    """
+    import torch
+    dt, N, d, V, K, loss_mask = _prep(h, W, topk_idx, topk_p, loss_mask)
+    dev = h.device
+    workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     dh = torch.empty((N, d), dtype=h.dtype, device=dev)
     dW = torch.empty((V, d), dtype=torch.float32, device=dev)
@@ -129,15 +154,98 @@ def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: boo
         row_loss = torch.empty(N, dtype=torch.float32, device=dev)
         row_lse = torch.empty(N, dtype=torch.float32, device=dev)
         zg = torch.empty((N, K), dtype=torch.float32, device=dev)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
     _check(_lib().kd_chunked_kl_fwd_bwd(
         _ptr(h), _ptr(W), dt, _ptr(topk_idx), _ptr(topk_p), _ptr(loss_mask), N, d, V, K, chunk,
         _ptr(loss), _ptr(dh), _ptr(dW), _ptr(row_loss), _ptr(row_lse), _ptr(zg),
-        _ptr(workspace), workspace.numel(), stream))
+        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
     if rows:
         return loss, dh, dW, row_loss, row_lse, zg
     return loss, dh, dW
+
+
+def fwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: bool = False,
+        workspace=None, stream=None):
+    """Forward half: (loss[1] f32, row_lse [N] f32) and, with ``rows``, also
+    (row_loss [N], zg [N, K]).  row_lse is the state ``bwd`` needs."""
+    import torch
+    dt, N, d, V, K, loss_mask = _prep(h, W, topk_idx, topk_p, loss_mask)
+    dev = h.device
+    workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    row_lse = torch.empty(N, dtype=torch.float32, device=dev)
+    row_loss = zg = None
+    if rows:
+        row_loss = torch.empty(N, dtype=torch.float32, device=dev)
+        zg = torch.empty((N, K), dtype=torch.float32, device=dev)
+    _check(_lib().kd_chunked_kl_fwd(
+        _ptr(h), _ptr(W), dt, _ptr(topk_idx), _ptr(topk_p), _ptr(loss_mask), N, d, V, K, chunk,
+        _ptr(loss), _ptr(row_lse), _ptr(row_loss), _ptr(zg), _ptr(workspace), workspace.numel(),
+        _stream(stream, dev)))
+    if rows:
+        return loss, row_lse, row_loss, zg
+    return loss, row_lse
+
+
+def bwd(h, W, topk_idx, topk_p, row_lse, grad_loss=None, loss_mask=None, chunk: int = 2048,
+        workspace=None, stream=None):
+    """Backward half: (dh [N, d] dtype, dW [V, d] f32) for the upstream gradient
+    ``grad_loss`` (a one-element float32 CUDA tensor; None means 1), recomputing the
+    logits from h and W with the ``row_lse`` saved by ``fwd``."""
+    import torch
+    dt, N, d, V, K, loss_mask = _prep(h, W, topk_idx, topk_p, loss_mask)
+    dev = h.device
+    if row_lse.dtype != torch.float32 or tuple(row_lse.shape) != (N,) or not row_lse.is_contiguous():
+        raise ValueError("row_lse must be a contiguous float32 tensor of shape [N]")
+    if grad_loss is None:
+        grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
+    grad_loss = grad_loss.reshape(1)
+    if grad_loss.dtype != torch.float32:
+        raise TypeError("grad_loss must be float32")
+    grad_loss = grad_loss.contiguous()
+    workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev)
+    dh = torch.empty((N, d), dtype=h.dtype, device=dev)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    _check(_lib().kd_chunked_kl_bwd(
+        _ptr(h), _ptr(W), dt, _ptr(topk_idx), _ptr(topk_p), _ptr(loss_mask), N, d, V, K, chunk,
+        _ptr(row_lse), _ptr(grad_loss), _ptr(dh), _ptr(dW), _ptr(workspace), workspace.numel(),
+        _stream(stream, dev)))
+    return dh, dW
+
+
+def _autograd_function():
+    import torch
+
+    class ChunkedKL(torch.autograd.Function):
+        """The loss as an autograd function of h and W: the forward keeps only the
+        per-token logsumexp; the backward recomputes the logits chunk by chunk."""
+
+        @staticmethod
+        def forward(ctx, h, W, topk_idx, topk_p, loss_mask, chunk):
+            loss, row_lse = fwd(h, W, topk_idx, topk_p, loss_mask, chunk)
+            ctx.save_for_backward(h, W, topk_idx, topk_p, loss_mask, row_lse)
+            ctx.chunk = chunk
+            return loss.view(())
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            h, W, topk_idx, topk_p, loss_mask, row_lse = ctx.saved_tensors
+            g = grad_out.detach().reshape(1).to(torch.float32).contiguous()
+            dh, dW = bwd(h, W, topk_idx, topk_p, row_lse, g, loss_mask, ctx.chunk)
+            # dW is float32; autograd converts it to W's dtype if they differ
+            return dh, dW, None, None, None, None
+
+    return ChunkedKL
+
+
+_CHUNKED_KL = None
+
+
+def chunked_kl_loss(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048):
+    """Mean top-K KL loss as a differentiable scalar of h and W (torch autograd)."""
+    global _CHUNKED_KL
+    if _CHUNKED_KL is None:
+        _CHUNKED_KL = _autograd_function()
+    return _CHUNKED_KL.apply(h, W, topk_idx, topk_p, loss_mask, chunk)
 
 
 def profile_enable(on: bool = True) -> None:

@@ -143,7 +143,7 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
 
 extern "C" {
 
-int kd_version(void) { return 1; }
+int kd_version(void) { return 2; }
 
 const char *kd_last_error(void) { return g_err; }
 
@@ -159,23 +159,40 @@ int kd_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk
   return KD_OK;
 }
 
-int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int32_t *topk_idx,
-                          const float *topk_p, const uint8_t *loss_mask, int64_t N, int64_t d,
-                          int64_t V, int32_t K, int64_t chunk, float *loss, void *dh, float *dW,
-                          float *row_loss, float *row_lse, float *zg, void *workspace,
-                          size_t workspace_bytes, void *stream_v) {
+}  // extern "C"
+
+namespace {
+
+// The three entry points share one routine.  FUSED: loss, dh, dW.  FWD: loss and the
+// per-token logsumexp (saved for BWD).  BWD: dh and dW from the saved logsumexp and an
+// upstream gradient g of the loss, with the logits recomputed chunk by chunk.
+enum Mode { M_FUSED, M_FWD, M_BWD };
+
+int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *topk_idx,
+        const float *topk_p, const uint8_t *loss_mask, int64_t N, int64_t d, int64_t V, int32_t K,
+        int64_t chunk, float *loss, void *dh, float *dW, float *row_loss, float *row_lse,
+        float *zg, const float *lse_in, const float *grad_loss, void *workspace,
+        size_t workspace_bytes, void *stream_v) {
   g_err[0] = 0;
   int rc = check_sizes(N, d, V, K, chunk, dtype);
   if (rc != KD_OK) return rc;
-  if (!W || !loss || !dW || !workspace) return fail(KD_E_ARG, "W, loss, dW and workspace are required");
-  if (N > 0 && (!h || !topk_idx || !topk_p || !dh))
-    return fail(KD_E_ARG, "h, topk_idx, topk_p and dh are required when N > 0");
+  const bool fwd = mode != M_BWD, bwd = mode != M_FWD;
+  if (!W || !workspace) return fail(KD_E_ARG, "W and workspace are required");
+  if (fwd && !loss) return fail(KD_E_ARG, "loss is required");
+  if (bwd && !dW) return fail(KD_E_ARG, "dW is required");
+  if (mode == M_BWD && !grad_loss) return fail(KD_E_ARG, "grad_loss is required");
+  if (N > 0 && (!h || !topk_idx || !topk_p))
+    return fail(KD_E_ARG, "h, topk_idx and topk_p are required when N > 0");
+  if (N > 0 && bwd && !dh) return fail(KD_E_ARG, "dh is required when N > 0");
+  if (N > 0 && mode == M_FWD && !row_lse)
+    return fail(KD_E_ARG, "row_lse is required (it is the state the backward call reads)");
+  if (N > 0 && mode == M_BWD && !lse_in) return fail(KD_E_ARG, "row_lse is required when N > 0");
   auto mis = [](const void *p, uintptr_t a) { return p && ((uintptr_t)p % a) != 0; };
   if (mis(h, 16) || mis(W, 16) || mis(dh, 16) || mis(dW, 16))
     return fail(KD_E_ARG, "h, W, dh and dW must be 16-byte aligned");
   if (mis(topk_idx, 4) || mis(topk_p, 4) || mis(loss, 4) || mis(row_loss, 4) ||
-      mis(row_lse, 4) || mis(zg, 4))
-    return fail(KD_E_ARG, "index, probability and float outputs must be 4-byte aligned");
+      mis(row_lse, 4) || mis(zg, 4) || mis(lse_in, 4) || mis(grad_loss, 4))
+    return fail(KD_E_ARG, "index, probability and float arguments must be 4-byte aligned");
   if (mis(workspace, 256)) return fail(KD_E_ARG, "workspace must be 256-byte aligned");
   kd::Layout L;
   kd::make_layout(N, d, V, K, chunk, dtype, &L);
@@ -202,8 +219,8 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
   const int64_t es = dtype == KD_BF16 ? 2 : 4;
 
   if (N == 0) {
-    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
-    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dW, (size_t)V * d * 4, stream));
+    if (fwd) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
+    if (bwd) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dW, (size_t)V * d * 4, stream));
     return KD_OK;
   }
 
@@ -224,15 +241,18 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
   const bool want_rows = row_loss || row_lse || zg;
 
   if (count == 0) {
-    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
-    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dW, (size_t)V * d * 4, stream));
-    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dh, (size_t)N * d * es, stream));
-    if (!want_rows) return KD_OK;
+    if (fwd) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
+    if (bwd) {
+      LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dW, (size_t)V * d * 4, stream));
+      LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dh, (size_t)N * d * es, stream));
+    }
+    if (!fwd || !want_rows) return KD_OK;
   }
+  const bool backward = bwd && count > 0;
   const float inv_count = count > 0 ? (float)(1.0 / (double)count) : 0.f;
-  LAUNCH(kd::KC_MISC, kd::launch_fill_zero(bcount, (size_t)L.nkeys * 4, stream));
+  if (fwd) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(bcount, (size_t)L.nkeys * 4, stream));
   void *WT = ws + L.off_wt;
-  if (count > 0 && dtype == KD_BF16)
+  if (backward && dtype == KD_BF16)
     LAUNCH(kd::KC_TRANSPOSE, kd::launch_transpose_w(W, V, d, L.V_pad, WT, stream));
 
   int chunk_i = 0;
@@ -243,19 +263,27 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
     const float *p_c = topk_p + c0 * K;
     const uint8_t *mask_c = loss_mask ? loss_mask + c0 : nullptr;
     float *zg_c = zg ? zg + c0 * K : zg_ws;
+    const float *lse_c = lse;
 
-    LAUNCH(kd::KC_BUCKET,
-           kd::launch_buckets(idx_c, rows, K, V, bcount, bcursor, boff, bent, stream));
-    LAUNCH(kd::KC_FWD_GEMM, kd::launch_fwd_gemm(dtype, W, h_c, rows, d, V, partials, L.C_alloc,
-                                                boff, bent, zg_c, K, stream));
-    LAUNCH(kd::KC_COMBINE,
-           kd::launch_combine(partials, L.n_lse, L.C_alloc, zg_c, p_c, mask_c, rows, K, inv_count,
-                              lse, sM, srow, rowterm, row_loss ? row_loss + c0 : nullptr,
-                              row_lse ? row_lse + c0 : nullptr, stream));
-    if (count == 0) continue;  // forward-only sweep for the per-row outputs
-    LAUNCH(kd::KC_MISC, kd::launch_accum_loss(rowterm, rows, acc, stream));
+    if (fwd) {
+      LAUNCH(kd::KC_BUCKET,
+             kd::launch_buckets(idx_c, rows, K, V, bcount, bcursor, boff, bent, stream));
+      LAUNCH(kd::KC_FWD_GEMM, kd::launch_fwd_gemm(dtype, W, h_c, rows, d, V, partials, L.C_alloc,
+                                                  boff, bent, zg_c, K, stream));
+      LAUNCH(kd::KC_COMBINE,
+             kd::launch_combine(partials, L.n_lse, L.C_alloc, zg_c, p_c, mask_c, rows, K, inv_count,
+                                lse, sM, srow, rowterm, row_loss ? row_loss + c0 : nullptr,
+                                row_lse ? row_lse + c0 : nullptr, stream));
+      if (count == 0) continue;  // forward-only sweep for the per-row outputs
+      LAUNCH(kd::KC_MISC, kd::launch_accum_loss(rowterm, rows, acc, stream));
+    } else {
+      lse_c = lse_in + c0;
+      LAUNCH(kd::KC_COMBINE, kd::launch_row_scale(p_c, mask_c, rows, K, inv_count, grad_loss, sM,
+                                                  srow, stream));
+    }
+    if (!backward) continue;
     LAUNCH(kd::KC_BWD_GEMM,
-           kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse, sM, dz, L.V_pad, L.C_alloc,
+           kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse_c, sM, dz, L.V_pad, L.C_alloc,
                                stream));
     LAUNCH(kd::KC_SCATTER,
            kd::launch_scatter(dtype, dz, L.C_alloc, idx_c, p_c, srow, rows, K, stream));
@@ -267,8 +295,39 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
            kd::launch_dw_gemm(dtype, dz, h_c, rows, d, V, L.V_pad, L.C_alloc, dW, chunk_i > 0,
                               stream));
   }
-  if (count > 0) LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));
+  if (fwd && count > 0) LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));
   return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int32_t *topk_idx,
+                          const float *topk_p, const uint8_t *loss_mask, int64_t N, int64_t d,
+                          int64_t V, int32_t K, int64_t chunk, float *loss, void *dh, float *dW,
+                          float *row_loss, float *row_lse, float *zg, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  return run(M_FUSED, h, W, dtype, topk_idx, topk_p, loss_mask, N, d, V, K, chunk, loss, dh, dW,
+             row_loss, row_lse, zg, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kd_chunked_kl_fwd(const void *h, const void *W, int32_t dtype, const int32_t *topk_idx,
+                      const float *topk_p, const uint8_t *loss_mask, int64_t N, int64_t d,
+                      int64_t V, int32_t K, int64_t chunk, float *loss, float *row_lse,
+                      float *row_loss, float *zg, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  return run(M_FWD, h, W, dtype, topk_idx, topk_p, loss_mask, N, d, V, K, chunk, loss, nullptr,
+             nullptr, row_loss, row_lse, zg, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kd_chunked_kl_bwd(const void *h, const void *W, int32_t dtype, const int32_t *topk_idx,
+                      const float *topk_p, const uint8_t *loss_mask, int64_t N, int64_t d,
+                      int64_t V, int32_t K, int64_t chunk, const float *row_lse,
+                      const float *grad_loss, void *dh, float *dW, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return run(M_BWD, h, W, dtype, topk_idx, topk_p, loss_mask, N, d, V, K, chunk, nullptr, dh, dW,
+             nullptr, nullptr, nullptr, row_lse, grad_loss, workspace, workspace_bytes, stream);
 }
 
 int kd_profile_enable(int on) {

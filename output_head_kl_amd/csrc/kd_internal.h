@@ -66,6 +66,10 @@ hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part
                           int64_t rows, int32_t K, float inv_count, float *lse, float *sM,
                           float *srow, double *rowterm, float *row_loss, float *row_lse,
                           hipStream_t s);
+// Backward-only path: sM = g*mask*M/count, s = g*mask/count per token (g on the device).
+hipError_t launch_row_scale(const float *p_c, const uint8_t *mask_c, int64_t rows, int32_t K,
+                            float inv_count, const float *g, float *sM, float *srow,
+                            hipStream_t s);
 hipError_t launch_accum_loss(const double *rowterm, int64_t rows, double *acc, hipStream_t s);
 hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s);
 // dz is stored as blocks of 256 vocabulary columns: element (c, v) at

@@ -1121,6 +1121,42 @@ hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part
   return hipGetLastError();
 }
 
+// Backward-only path: per token, sM = g * mask * M / count and s = g * mask / count,
+// with M = sum_k p summed in float64 in exactly the order k_combine uses (wave w takes
+// k = w, w+16, ...; the 16 wave sums are added in wave order), so that with g = 1 the
+// backward matches the fused call bit for bit.  g is read from device memory.
+__global__ __launch_bounds__(64 * kCombWaves) void k_row_scale(const float *p,
+                                                               const uint8_t *mask, int rows,
+                                                               int K, float inv_count,
+                                                               const float *g, float *sM_out,
+                                                               float *s_out) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = blockIdx.x * 64 + lane;
+  const bool live = r < rows;
+  double Ms = 0.0;
+  if (live)
+    for (int k = w; k < K; k += kCombWaves) Ms += (double)p[(long long)r * K + k];
+  __shared__ double sd[kCombWaves][64];
+  sd[w][lane] = Ms;
+  __syncthreads();
+  if (w == 0 && live) {
+    double ms = 0.0;
+    for (int i = 0; i < kCombWaves; ++i) ms += sd[i][lane];
+    const bool on = mask ? mask[r] != 0 : true;
+    const float gg = g[0];
+    sM_out[r] = on ? (float)(ms * (double)inv_count) * gg : 0.f;
+    s_out[r] = on ? inv_count * gg : 0.f;
+  }
+}
+
+hipError_t launch_row_scale(const float *p_c, const uint8_t *mask_c, int64_t rows, int32_t K,
+                            float inv_count, const float *g, float *sM, float *srow,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(k_row_scale, dim3(cdiv(rows, 64)), dim3(64 * kCombWaves), 0, s, p_c, mask_c,
+                     (int)rows, (int)K, inv_count, g, sM, srow);
+  return hipGetLastError();
+}
+
 // acc[0] += sum of rowterm[0..rows) in a fixed order (deterministic).
 __global__ void k_accum_loss(const double *rowterm, int rows, double *acc) {
   __shared__ double sh[256];

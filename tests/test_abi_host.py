@@ -106,3 +106,57 @@ def test_workspace_too_small_reports_needed_size(lib):
     need = kd.workspace_bytes(64, 64, 1000, 4, 32)
     assert _call(lib, wsb=need - 1) == E_WORKSPACE
     assert str(need).encode() in lib.kd_last_error()
+
+
+def _call_fwd(lib, **kw):
+    base = dict(h=0x100000, W=0x200000, dtype=1, idx=0x300000, p=0x400000, mask=None, N=64,
+                d=64, V=1000, K=4, chunk=32, loss=0x500000, row_lse=0x900000, row_loss=None,
+                zg=None, ws=0x800000, wsb=1 << 40, stream=None)
+    base.update(kw)
+    b = base
+    return lib.kd_chunked_kl_fwd(b["h"], b["W"], b["dtype"], b["idx"], b["p"], b["mask"],
+                                 b["N"], b["d"], b["V"], b["K"], b["chunk"], b["loss"],
+                                 b["row_lse"], b["row_loss"], b["zg"], b["ws"], b["wsb"],
+                                 b["stream"])
+
+
+def _call_bwd(lib, **kw):
+    base = dict(h=0x100000, W=0x200000, dtype=1, idx=0x300000, p=0x400000, mask=None, N=64,
+                d=64, V=1000, K=4, chunk=32, row_lse=0x900000, g=0xA00000, dh=0x600000,
+                dW=0x700000, ws=0x800000, wsb=1 << 40, stream=None)
+    base.update(kw)
+    b = base
+    return lib.kd_chunked_kl_bwd(b["h"], b["W"], b["dtype"], b["idx"], b["p"], b["mask"],
+                                 b["N"], b["d"], b["V"], b["K"], b["chunk"], b["row_lse"],
+                                 b["g"], b["dh"], b["dW"], b["ws"], b["wsb"], b["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(loss=None), E_ARG),
+    (dict(row_lse=None), E_ARG),     # the state the backward reads is required
+    (dict(W=None), E_ARG),
+    (dict(h=None), E_ARG),
+    (dict(row_lse=0x900002), E_ARG),
+    (dict(h=0x100008), E_ARG),
+    (dict(d=60), E_UNSUPPORTED),
+    (dict(wsb=1000), E_WORKSPACE),
+])
+def test_forward_entry_rejects_bad_calls_on_host(lib, kw, code):
+    assert _call_fwd(lib, **kw) == code
+    assert lib.kd_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(row_lse=None), E_ARG),
+    (dict(g=None), E_ARG),
+    (dict(dh=None), E_ARG),
+    (dict(dW=None), E_ARG),
+    (dict(g=0xA00002), E_ARG),
+    (dict(dW=0x700004), E_ARG),
+    (dict(d=60), E_UNSUPPORTED),
+    (dict(K=0), E_ARG),
+    (dict(wsb=1000), E_WORKSPACE),
+])
+def test_backward_entry_rejects_bad_calls_on_host(lib, kw, code):
+    assert _call_bwd(lib, **kw) == code
+    assert lib.kd_last_error()
