@@ -43,7 +43,7 @@ import numpy as np
 BASE_SEED = 20260804
 
 # Component ids for the per-component streams.
-_H, _W, _IDX, _SCORES, _MASS, _LENGTHS, _SUBSET = range(7)
+_H, _W, _IDX, _SCORES, _MASS, _LENGTHS, _SUBSET, _TEACHER = range(8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -294,3 +294,43 @@ def take_rows(inp: Inputs, rows: np.ndarray) -> Inputs:
     return Inputs(cfg, inp.seed, np.ascontiguousarray(inp.h[rows]), inp.W,
                   np.ascontiguousarray(inp.idx[rows]), np.ascontiguousarray(inp.p[rows]),
                   np.ascontiguousarray(inp.mask[rows]))
+
+
+# --------------------------------------------------------------------------
+# Teacher logits (input of the top-K cache producer)
+# --------------------------------------------------------------------------
+def make_teacher_logits(N: int, V: int, seed: int, dtype: str = "bf16", row_lo: int = 0,
+                        row_hi: Optional[int] = None, sigma: float = 2.0,
+                        alpha: float = 1.0, threads: int = 8) -> np.ndarray:
+    """Rows ``[row_lo, row_hi)`` of synthetic teacher logits
+    ``t[n, v] = sigma * N(0, 1) - alpha * log(v + 1)``.
+
+    The ``-alpha log(v+1)`` term is a token-frequency prior (low token ids are the
+    frequent ones, as with the Zipf-drawn cache indices), so each row's top tokens
+    concentrate at low ids while the rest of the vocabulary is a Gaussian tail.
+    Every row is drawn from its own stream, so any row subset is reproducible
+    cheaply.  bf16 logits are returned as uint16 bits (rounded once, RNE), whose
+    many exactly equal values exercise the tie rule of the top-K selection.
+    """
+    row_hi = N if row_hi is None else row_hi
+    prior = (-alpha * np.log1p(np.arange(V, dtype=np.float64))).astype(np.float32)
+    out = np.empty((row_hi - row_lo, V), dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def fill(r0, r1):
+        for r in range(r0, r1):
+            g = np.random.default_rng([seed, _TEACHER, r])
+            x = g.standard_normal(V, dtype=np.float32)
+            x *= np.float32(sigma)
+            x += prior
+            out[r - row_lo] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+    n = row_hi - row_lo
+    if n <= 64 or threads <= 1:
+        fill(row_lo, row_hi)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        step = (n + threads - 1) // threads
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda i: fill(row_lo + i * step, min(row_hi, row_lo + (i + 1) * step)),
+                        range(threads)))
+    return out

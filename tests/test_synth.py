@@ -65,3 +65,16 @@ def test_packed_masks(cid):
     else:
         frac = 1 - m.mean()
         assert 0.09 < frac < 0.115
+
+
+def test_teacher_logits_rows_are_reproducible_and_shaped():
+    a = synth.make_teacher_logits(300, 1000, seed=5)
+    b = synth.make_teacher_logits(300, 1000, seed=5, row_lo=120, row_hi=130, threads=1)
+    assert a.dtype == np.uint16 and a.shape == (300, 1000)
+    assert np.array_equal(a[120:130], b)
+    f = synth.make_teacher_logits(4, 1000, seed=5, dtype="f32")
+    assert f.dtype == np.float32
+    # the frequency prior puts the largest logits at low token ids on average
+    x = synth.bf16_bits_to_f32(a).astype(np.float64)
+    top = np.argsort(-x, axis=1, kind="stable")[:, :10]
+    assert np.median(top) < 200
