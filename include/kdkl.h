@@ -149,6 +149,33 @@ int kd_chunked_kl_bwd(const void *h, const void *W, int32_t dtype,
                       void *dh, float *dW,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kd_teacher_topk -- the teacher top-K cache producer.
+ *
+ * The offline step that runs the teacher once and keeps, per position, its most
+ * likely tokens with their scores (thorstenmeyerai.com article, TL;DR and
+ * infographic "Select top 100", "Write cache"), as the probabilities the loss
+ * reads (aimodeling.com article, "First cut").  For every row n of teacher logits:
+ *   row_lse[n]    = log sum_v exp t[n,v]                      (optional, NULL = skip)
+ *   topk_idx[n,k] = the K tokens with the largest logits, in decreasing order of
+ *                   logit; equal logits in increasing token order (+0.0 == -0.0)
+ *   topk_p[n,k]   = exp(t[n, topk_idx[n,k]] - row_lse[n])  (full-softmax
+ *                   probability; the K values are not renormalised)
+ * Device pointers, caller-owned, row-major:
+ *   logits   [N, V]  dtype (KD_BF16 or KD_F32), aligned to its element size
+ *   topk_idx [N, K]  int32;  topk_p [N, K] float32;  row_lse [N] float32 or NULL
+ *   workspace        >= kd_topk_workspace_bytes() bytes, 256-byte aligned
+ * Sizes: N >= 0, 1 <= K <= min(V, 256), V < 2^31, N < 2^31.
+ * Each row is read from device memory once.  The call synchronises the stream once,
+ * at the end, to read the validity flag: a row with a NaN or +inf logit, or with no
+ * finite logit, gives KD_E_INDEX and the outputs are undefined.  Other errors are
+ * host-side checks made before any device work.
+ */
+int kd_topk_workspace_bytes(size_t *bytes_out);
+int kd_teacher_topk(const void *logits, int32_t dtype, int64_t N, int64_t V, int32_t K,
+                    int32_t *topk_idx, float *topk_p, float *row_lse,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Text describing the last non-OK return on the calling thread ("" if none). */
 const char *kd_last_error(void);
 

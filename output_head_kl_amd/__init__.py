@@ -13,7 +13,7 @@ import os
 from typing import Optional
 
 __all__ = ["KDError", "library_path", "workspace_bytes", "fwd_bwd", "fwd", "bwd",
-           "chunked_kl_loss", "profile_enable", "profile_read", "profile_classes", "KD_F32",
+           "chunked_kl_loss", "teacher_topk", "profile_enable", "profile_read", "profile_classes", "KD_F32",
            "KD_BF16"]
 
 KD_F32, KD_BF16 = 0, 1
@@ -54,6 +54,10 @@ def _lib():
     lib.kd_chunked_kl_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
                                       vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_bwd.restype = ctypes.c_int
+    lib.kd_topk_workspace_bytes.argtypes = [ctypes.POINTER(sz)]
+    lib.kd_topk_workspace_bytes.restype = ctypes.c_int
+    lib.kd_teacher_topk.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, sz, vp]
+    lib.kd_teacher_topk.restype = ctypes.c_int
     lib.kd_last_error.argtypes = []
     lib.kd_last_error.restype = ctypes.c_char_p
     lib.kd_version.restype = ctypes.c_int
@@ -246,6 +250,27 @@ def chunked_kl_loss(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048):
     if _CHUNKED_KL is None:
         _CHUNKED_KL = _autograd_function()
     return _CHUNKED_KL.apply(h, W, topk_idx, topk_p, loss_mask, chunk)
+
+
+def teacher_topk(logits, K: int = 100, lse: bool = True, workspace=None, stream=None):
+    """Teacher top-K cache for ``logits`` [N, V] (bfloat16 or float32 CUDA tensor):
+    ``(topk_idx [N, K] int32, topk_p [N, K] float32[, row_lse [N] float32])``."""
+    import torch
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [N, V] tensor")
+    dt = _dtype_code(logits)
+    N, V = logits.shape
+    dev = logits.device
+    if workspace is None:
+        out = ctypes.c_size_t(0)
+        _check(_lib().kd_topk_workspace_bytes(ctypes.byref(out)))
+        workspace = torch.empty(int(out.value), dtype=torch.uint8, device=dev)
+    idx = torch.empty((N, K), dtype=torch.int32, device=dev)
+    p = torch.empty((N, K), dtype=torch.float32, device=dev)
+    row_lse = torch.empty(N, dtype=torch.float32, device=dev) if lse else None
+    _check(_lib().kd_teacher_topk(_ptr(logits), dt, N, V, K, _ptr(idx), _ptr(p), _ptr(row_lse),
+                                  _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return (idx, p, row_lse) if lse else (idx, p)
 
 
 def profile_enable(on: bool = True) -> None:

@@ -5,7 +5,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = [os.path.join(PKG, "csrc", f) for f in ("kd_kernels.hip", "kd_api.hip")]
+SRC = [os.path.join(PKG, "csrc", f) for f in ("kd_kernels.hip", "kd_api.hip", "kd_topk.hip")]
 OUT = os.path.join(PKG, "libkdkl.so")
 
 FLAGS = [

@@ -41,7 +41,7 @@ std::mutex g_prof_mu;
 
 const char *const kClassNames[kd::KC_COUNT] = {
     "validate", "fwd_gemm_lse", "bucket", "combine_lse_loss", "bwd_gemm_dz",
-    "scatter",  "dh_gemm",      "dh_reduce", "dw_gemm",      "w_transpose", "misc"};
+    "scatter",  "dh_gemm",      "dh_reduce", "dw_gemm",      "w_transpose", "teacher_topk", "misc"};
 
 #define HIPCHK(expr)                                                                 \
   do {                                                                               \
@@ -328,6 +328,44 @@ int kd_chunked_kl_bwd(const void *h, const void *W, int32_t dtype, const int32_t
                       size_t workspace_bytes, void *stream) {
   return run(M_BWD, h, W, dtype, topk_idx, topk_p, loss_mask, N, d, V, K, chunk, nullptr, dh, dW,
              nullptr, nullptr, nullptr, row_lse, grad_loss, workspace, workspace_bytes, stream);
+}
+
+int kd_topk_workspace_bytes(size_t *bytes_out) {
+  g_err[0] = 0;
+  if (!bytes_out) return fail(KD_E_ARG, "bytes_out is NULL");
+  *bytes_out = 256;
+  return KD_OK;
+}
+
+int kd_teacher_topk(const void *logits, int32_t dtype, int64_t N, int64_t V, int32_t K,
+                    int32_t *topk_idx, float *topk_p, float *row_lse, void *workspace,
+                    size_t workspace_bytes, void *stream_v) {
+  g_err[0] = 0;
+  if (dtype != KD_F32 && dtype != KD_BF16) return fail(KD_E_ARG, "dtype %d unknown", dtype);
+  if (N < 0 || V < 1 || K < 1) return fail(KD_E_ARG, "need N >= 0, V >= 1, K >= 1");
+  if (K > V) return fail(KD_E_ARG, "K = %d exceeds V = %lld", K, (long long)V);
+  if (K > kd::kTopkMaxK) return fail(KD_E_UNSUPPORTED, "K = %d above %d", K, kd::kTopkMaxK);
+  if (V >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+    return fail(KD_E_UNSUPPORTED, "V and N must be below 2^31");
+  if (N > 0 && (!logits || !topk_idx || !topk_p)) return fail(KD_E_ARG, "logits, topk_idx and topk_p are required");
+  if (!workspace) return fail(KD_E_ARG, "workspace is required");
+  const size_t es = dtype == KD_BF16 ? 2 : 4;
+  if (logits && (uintptr_t)logits % es) return fail(KD_E_ARG, "logits misaligned");
+  if (((uintptr_t)topk_idx | (uintptr_t)topk_p | (uintptr_t)row_lse) % 4)
+    return fail(KD_E_ARG, "outputs must be 4-byte aligned");
+  if ((uintptr_t)workspace % 256) return fail(KD_E_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < 256) return fail(KD_E_WORKSPACE, "workspace has %zu bytes, needs 256", workspace_bytes);
+  if (N == 0) return KD_OK;
+  hipStream_t stream = (hipStream_t)stream_v;
+  int *flags = (int *)workspace;
+  LAUNCH(kd::KC_MISC, kd::launch_fill_zero(flags, 64, stream));
+  LAUNCH(kd::KC_TOPK, kd::launch_teacher_topk(dtype, logits, N, V, K, topk_idx, topk_p, row_lse,
+                                              flags, stream));
+  int hf = 0;
+  HIPCHK(hipMemcpyAsync(&hf, flags, sizeof hf, hipMemcpyDeviceToHost, stream));
+  HIPCHK(hipStreamSynchronize(stream));
+  if (hf) return fail(KD_E_INDEX, "a row has a NaN or +inf logit or no finite logit; outputs undefined");
+  return KD_OK;
 }
 
 int kd_profile_enable(int on) {

@@ -25,6 +25,7 @@ enum KClass {
   KC_DH_REDUCE,    // dh partials summed and rounded
   KC_DW_GEMM,      // dW accumulation
   KC_TRANSPOSE,    // W copied to vocabulary-contiguous blocks for the dh GEMM
+  KC_TOPK,         // teacher top-K cache producer
   KC_MISC,         // fills, loss accumulation and finalisation
   KC_COUNT
 };
@@ -93,6 +94,13 @@ hipError_t launch_dh_reduce(int dtype, const float *part, int nsplit, int64_t C_
 hipError_t launch_dw_gemm(int dtype, const void *dz, const void *h_c, int64_t rows, int64_t d,
                           int64_t V, int64_t V_pad, int64_t C_alloc, float *dW, int accumulate,
                           hipStream_t s);
+
+// --- teacher top-K cache producer (kd_topk.hip) ---
+constexpr int kTopkMaxK = 256;
+// One workgroup per row; flags[0] |= 1 for a row with a NaN or +inf logit or with no
+// finite logit.  lse may be null.
+hipError_t launch_teacher_topk(int dtype, const void *logits, int64_t N, int64_t V, int32_t K,
+                               int32_t *idx, float *p, float *lse, int *flags, hipStream_t s);
 
 // --- timing hooks (kd_api.hip) ---
 void prof_begin(int cls, hipStream_t s);

@@ -632,8 +632,9 @@ __device__ __forceinline__ void wait_vm() {
 
 // WN = waves along n: 2 gives 4 waves of 128 x 128 (one per SIMD, 256 accumulators
 // each), 4 gives 8 waves of 128 x 64 (two per SIMD, so one wave's MFMAs cover the
-// other's waits).
-template <int AK, int BKIND, class Epi, int NST = 5, int BK = 32, int WN = 2>
+// other's waits).  NSTA / NSTB = LDS slots of the A / B rings; A may have one slot
+// more than B, giving the operand streamed from HBM one more stage of lookahead.
+template <int AK, int BKIND, class Epi, int NSTA, int NSTB, int BK, int WN>
 __global__ __attribute__((amdgpu_flat_work_group_size(128 * WN, 128 * WN),
                           amdgpu_waves_per_eu(WN / 2, WN / 2)))
 void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
@@ -648,7 +649,9 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
   constexpr int NMF = 4 * NCB;          // MFMAs per wave per substep
   // LDS reads per substep: one per fragment, two per transposed (MC) fragment
   constexpr int NRD = 4 * (AK == OP_MC ? 2 : 1) + NCB * (BKIND == OP_MC ? 2 : 1);
-  __shared__ __attribute__((aligned(1024))) char smem[NST * GG::STAGE];
+  static_assert(NSTB >= 2 && (NSTA == NSTB || NSTA == NSTB + 1), "ring shapes");
+  __shared__ __attribute__((aligned(1024))) char smem[(NSTA + NSTB) * GG::OPB];
+  char *const smemB = smem + NSTA * GG::OPB;
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per_split = G.ntm * G.ntn;
@@ -683,34 +686,37 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
 #pragma unroll
     for (int j = 0; j < NCB; ++j) acc[i][j] = f32x16{};
 
-  // Prologue: every slot loading (stages past the end are all-zero loads, so the
-  // count of loads in flight is the same in every iteration); stage 0 landed.
-  for (int s = 0; s < NST; ++s) {
-    Loader<AK, NI>::issue(Ak, ca, m0, kb + s * BK, smem + s * GG::STAGE, w);
-    Loader<BKIND, NI>::issue(Bk, cb, n0, kb + s * BK, smem + s * GG::STAGE + GG::OPB, w);
+  // Prologue: every slot loading, in the order A0 B0 A1 B1 [A2] (stages past the end
+  // are all-zero loads, so the count of loads in flight is the same in every
+  // iteration); then stage 0 landed.
+  for (int s = 0; s < NSTA; ++s) {
+    Loader<AK, NI>::issue(Ak, ca, m0, kb + s * BK, smem + s * GG::OPB, w);
+    if (s < NSTB) Loader<BKIND, NI>::issue(Bk, cb, n0, kb + s * BK, smemB + s * GG::OPB, w);
   }
-  wait_vm<LPS * (NST - 1), false>();
+  wait_vm<NI * (NSTA + NSTB - 2), false>();
   __syncthreads();
 
   bf16x8 fa[2][4], fb[2][NCB];
 #pragma unroll
   for (int i = 0; i < 4; ++i) fa[0][i] = PFrag<AK, BK>::load(smem, wr * 128 + i * 32, 0, lane);
 #pragma unroll
-  for (int j = 0; j < NCB; ++j) fb[0][j] = PFrag<BKIND, BK>::load(smem + GG::OPB, wc * WNC + j * 32, 0, lane);
+  for (int j = 0; j < NCB; ++j) fb[0][j] = PFrag<BKIND, BK>::load(smemB, wc * WNC + j * 32, 0, lane);
 
-  int bcur = 0;  // ring slot of stage it
+  int acur = 0, bcur = 0;  // ring slots of stage it
   for (int it = 0; it < nk; ++it) {
-    const int bnext = bcur + 1 == NST ? 0 : bcur + 1;
-    char *cur = smem + bcur * GG::STAGE;
+    const int anext = acur + 1 == NSTA ? 0 : acur + 1;
+    const int bnext = bcur + 1 == NSTB ? 0 : bcur + 1;
+    char *cura = smem + acur * GG::OPB;
+    char *curb = smemB + bcur * GG::OPB;
 #pragma unroll
     for (int ss = 0; ss < S - 1; ++ss) {
       // substep ss on registers [ss&1]; read substep ss+1 meanwhile
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        fa[(ss + 1) & 1][i] = PFrag<AK, BK>::load(cur, wr * 128 + i * 32, ss + 1, lane);
+        fa[(ss + 1) & 1][i] = PFrag<AK, BK>::load(cura, wr * 128 + i * 32, ss + 1, lane);
 #pragma unroll
       for (int j = 0; j < NCB; ++j)
-        fb[(ss + 1) & 1][j] = PFrag<BKIND, BK>::load(cur + GG::OPB, wc * WNC + j * 32, ss + 1, lane);
+        fb[(ss + 1) & 1][j] = PFrag<BKIND, BK>::load(curb, wc * WNC + j * 32, ss + 1, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -725,20 +731,23 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
     }
 
     // Stage it+1 must have landed for every wave, and every wave must hold the whole of
-    // stage it in registers or accumulators, since its slot is refilled next.
-    wait_vm<LPS * (NST - 2), true>();
+    // stage it in registers or accumulators, since its slots are refilled next.  Loads
+    // are issued B(j+NSTB) then A(j+NSTA) in iteration j, so what may still be in
+    // flight here is A(it+2) when A has the extra slot, else nothing.
+    wait_vm<NI * (NSTA - NSTB), true>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
     // last substep on registers [(S-1)&1]; meanwhile read substep 0 of stage it+1 and
-    // refill this slot with stage it+NST
-    const char *nx = smem + bnext * GG::STAGE;
+    // refill this stage's slots with B(it+NSTB) and A(it+NSTA)
+    const char *nxa = smem + anext * GG::OPB;
+    const char *nxb = smemB + bnext * GG::OPB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = PFrag<AK, BK>::load(nx, wr * 128 + i * 32, 0, lane);
+    for (int i = 0; i < 4; ++i) fa[0][i] = PFrag<AK, BK>::load(nxa, wr * 128 + i * 32, 0, lane);
 #pragma unroll
-    for (int j = 0; j < NCB; ++j) fb[0][j] = PFrag<BKIND, BK>::load(nx + GG::OPB, wc * WNC + j * 32, 0, lane);
-    Loader<AK, NI>::issue(Ak, ca, m0, kb + (it + NST) * BK, cur, w);
-    Loader<BKIND, NI>::issue(Bk, cb, n0, kb + (it + NST) * BK, cur + GG::OPB, w);
+    for (int j = 0; j < NCB; ++j) fb[0][j] = PFrag<BKIND, BK>::load(nxb, wc * WNC + j * 32, 0, lane);
+    Loader<BKIND, NI>::issue(Bk, cb, n0, kb + (it + NSTB) * BK, curb, w);
+    Loader<AK, NI>::issue(Ak, ca, m0, kb + (it + NSTA) * BK, cura, w);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -758,6 +767,7 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
       __builtin_amdgcn_sched_group_barrier(KD_SG_VALU, 2, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
+    acur = anext;
     bcur = bnext;
   }
   wait_vm<0, false>();  // the zero loads issued past the end
@@ -772,7 +782,7 @@ static hipError_t run_gemm(const Operand &A, const Operand &B, const GemmGrid &G
   // 8 waves (two per SIMD), two LDS stages of 64 k: a KC operand row is then one
   // 128-byte segment per stage, which halves the memory requests of k-contiguous operands
   if constexpr (DT == 1)
-    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKIND, Epi, 2, 64, 4>), dim3((unsigned)T), dim3(512),
+    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKIND, Epi, 2, 2, 64, 4>), dim3((unsigned)T), dim3(512),
                        0, s, A, B, G, epi);
   else
     hipLaunchKernelGGL((gemm_kernel<DT, AK, BKIND, Epi>), dim3((unsigned)T), dim3(256), 0, s, A,

@@ -1,0 +1,338 @@
+// Teacher top-K cache producer on gfx950: for every row of teacher logits, the K
+// most likely tokens with their probabilities under the full softmax, and the
+// row's logsumexp.  The offline step runs the teacher once and keeps its top 100
+// tokens and scores per position (thorstenmeyerai.com article, TL;DR and infographic
+// "Select top 100"); the loss reads them as probabilities (aimodeling.com article,
+// "First cut").
+//
+// One workgroup (4 waves) per row reads the row from HBM exactly once:
+//  * streaming pass: 16-byte loads per lane; an online (max, sum exp) per lane for the
+//    logsumexp; every element whose order-preserving key reaches the running
+//    threshold is appended to an LDS candidate buffer (one LDS atomic per wave per
+//    chunk);
+//  * every GROUP chunks, if the buffer could overflow on the next group, a radix select
+//    over the buffer keeps exactly the K best candidates and raises the threshold;
+//  * the selection key is unique: (value key << 32) | ~index, so equal logits are
+//    ordered by increasing token index and the result does not depend on timing;
+//  * at the end a last radix select leaves exactly K entries, each finds its rank
+//    among them, and the outputs are written in decreasing order.
+#include "kd_internal.h"
+
+#include <cstdint>
+
+namespace kd {
+
+namespace {
+
+constexpr float kTkLog2e = 1.4426950408889634f;
+constexpr float kTkLn2 = 0.6931471805599453f;
+constexpr int kTkThreads = 256;
+
+// Order-preserving 32-bit key of a float (larger float -> larger key); -0.0 is +0.0.
+__device__ __forceinline__ uint32_t f_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int DT> struct TkT;
+template <> struct TkT<1> {  // bf16 logits: 16-bit value keys, 8 elements per load
+  static constexpr int VB = 16, EPL = 8;
+  static __device__ __forceinline__ uint32_t vkey(float x) { return f_key(x) >> 16; }
+  static __device__ __forceinline__ float value(uint32_t k) {
+    const uint32_t u = (k & 0x8000u) ? ((k & 0x7FFFu) << 16) : ((~k & 0xFFFFu) << 16);
+    return __uint_as_float(u);
+  }
+  static __device__ __forceinline__ float load1(const void *p, long long i) {
+    return __uint_as_float((uint32_t)((const unsigned short *)p)[i] << 16);
+  }
+  static __device__ __forceinline__ void load_vec(const void *p, long long i, float (&x)[8]) {
+    const uint4 v = *(const uint4 *)((const unsigned short *)p + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct TkT<0> {  // fp32 logits: 32-bit value keys, 4 elements per load
+  static constexpr int VB = 32, EPL = 4;
+  static __device__ __forceinline__ uint32_t vkey(float x) { return f_key(x); }
+  static __device__ __forceinline__ float value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+  }
+  static __device__ __forceinline__ float load1(const void *p, long long i) {
+    return ((const float *)p)[i];
+  }
+  static __device__ __forceinline__ void load_vec(const void *p, long long i, float (&x)[4]) {
+    const float4 v = *(const float4 *)((const float *)p + i);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+};
+
+// Composite selection key: value key, then the complemented index (smaller index wins).
+__device__ __forceinline__ uint64_t comp_key(uint32_t vk, uint32_t idx) {
+  return ((uint64_t)vk << 32) | (uint32_t)~idx;
+}
+
+// Block-wide: among s_ck[0..n) (unique composite keys of TB significant bits), find
+// (P, D) such that exactly `need` entries have (key >> (TB - D)) >= P.  Digits of 8
+// bits from the top; stops as soon as the selected digit's whole bin is needed.
+template <int TB>
+__device__ void radix_select(const uint64_t *s_ck, int n, int need, uint32_t *s_hist,
+                             uint64_t *s_res, int t) {
+  uint64_t P = 0;
+  int D = 0;
+  __shared__ int s_bin, s_above, s_inbin;
+  for (int level = 0; level < TB / 8; ++level) {
+    const int shift = TB - 8 * (level + 1);
+    s_hist[t] = 0u;
+    __syncthreads();
+    // entries whose digits above this level equal the prefix (at the first level of a
+    // 64-bit key every entry matches: a shift by 64 would be undefined)
+    const bool all = shift + 8 >= 64;
+    for (int i = t; i < n; i += kTkThreads) {
+      const uint64_t c = s_ck[i];
+      if (all || (c >> (shift + 8)) == P) atomicAdd(&s_hist[(c >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // suffix sums over the 256 bins: wave w holds bins 64w..64w+63
+    const int lane = t & 63, w = t >> 6;
+    const uint32_t h = s_hist[t];
+    uint32_t sfx = h;  // inclusive suffix within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_down(sfx, o, 64);
+      if (lane + o < 64) sfx += y;
+    }
+    __shared__ uint32_t s_wtot[4];
+    if (lane == 0) s_wtot[w] = sfx;
+    __syncthreads();
+    uint32_t later = 0;
+    for (int w2 = w + 1; w2 < 4; ++w2) later += s_wtot[w2];
+    const uint32_t S = sfx + later;  // entries of this prefix with digit >= t
+    if (S >= (uint32_t)need && S - h < (uint32_t)need) {
+      s_bin = t;
+      s_above = (int)(S - h);
+      s_inbin = (int)h;
+    }
+    __syncthreads();
+    const int bin = s_bin, above = s_above, inbin = s_inbin;
+    need -= above;
+    P = (P << 8) | (uint64_t)bin;
+    D += 8;
+    __syncthreads();  // s_bin and friends are rewritten by the next level
+    if (inbin == need) break;
+  }
+  if (t == 0) {
+    s_res[0] = P;
+    s_res[1] = (uint64_t)D;
+  }
+  __syncthreads();
+}
+
+// Keeps the entries selected by (P, D) at the front of the buffer (order arbitrary).
+// Every thread first takes its entries into registers, so the rewrite cannot
+// overwrite an entry not yet read.
+template <int TB, int CAP>
+__device__ int compact(uint64_t *s_ck, int n, uint64_t P, int D, int *s_cnt, int t) {
+  constexpr int PER = (CAP + kTkThreads - 1) / kTkThreads;
+  uint64_t mine[PER];
+  bool sel[PER];
+  int nm = 0;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int i = t + r * kTkThreads;
+    mine[r] = i < n ? s_ck[i] : 0ull;
+    sel[r] = i < n && (mine[r] >> (TB - D)) >= P;
+    nm += sel[r] ? 1 : 0;
+  }
+  __syncthreads();
+  if (t == 0) *s_cnt = 0;
+  __syncthreads();
+  int slot = nm ? atomicAdd(s_cnt, nm) : 0;
+#pragma unroll
+  for (int r = 0; r < PER; ++r)
+    if (sel[r]) s_ck[slot++] = mine[r];
+  __syncthreads();
+  return *s_cnt;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits, long long V,
+                                                             int K, int32_t *idx_out,
+                                                             float *p_out, float *lse_out,
+                                                             int *flags) {
+  using T = TkT<DT>;
+  constexpr int EPL = VEC ? T::EPL : 1;
+  constexpr int CHUNK = kTkThreads * EPL;
+  constexpr int GROUP = DT == 1 ? 2 : 4;                 // chunks between checkpoints
+  constexpr int CAP = kTopkMaxK + GROUP * CHUNK;         // never overflows (see below)
+  constexpr int TB = T::VB + 32;
+  __shared__ uint64_t s_ck[CAP];
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint64_t s_res[2];
+  __shared__ int s_cnt;
+  __shared__ float s_m[kTkThreads / 64];
+  __shared__ double s_s[kTkThreads / 64];
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const long long row = blockIdx.x;
+  const char *rp = (const char *)logits + row * V * (DT == 1 ? 2 : 4);
+  if (t == 0) s_cnt = 0;
+  __syncthreads();
+
+  uint64_t tge = 0;  // candidate iff value key >= tge (tge may be 2^VB: nothing passes)
+  // running max and sum of exp(x - max) per lane; the sum is kept in float64 (a row
+  // has ~V/256 terms per lane), each term is a float32 exp2
+  float m = -INFINITY;
+  double s = 0.0;
+  int bad = 0;
+  const long long nchunks = (V + CHUNK - 1) / CHUNK;
+  for (long long ci = 0; ci < nchunks; ++ci) {
+    const long long e0 = ci * CHUNK + (long long)t * EPL;
+    float x[EPL];
+    bool ok[EPL];
+    if (VEC && e0 + EPL <= V) {
+      if constexpr (VEC) T::load_vec(rp, e0, x);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) ok[j] = true;
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        ok[j] = e0 + j < V;
+        x[j] = ok[j] ? T::load1(rp, e0 + j) : -INFINITY;
+      }
+    }
+    // online logsumexp of this lane; NaN and +inf are errors
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      bad |= (x[j] != x[j]) | (x[j] == INFINITY);
+      lm = fmaxf(lm, x[j]);
+    }
+    if (lm > m) {
+      s = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f((m - lm) * kTkLog2e);
+      m = lm;
+    }
+    if (m != -INFINITY) {
+      float part = 0.f;  // at most 8 terms in float32
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) part += __builtin_amdgcn_exp2f((x[j] - m) * kTkLog2e);
+      s += (double)part;
+    }
+    // candidates: one LDS atomic per wave
+    uint32_t vk[EPL];
+    int mycnt = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      vk[j] = T::vkey(x[j]);
+      mycnt += (ok[j] && (uint64_t)vk[j] >= tge) ? 1 : 0;
+    }
+    int incl = mycnt;  // inclusive prefix over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const int wtot = __shfl(incl, 63, 64);
+    int wbase = 0;
+    if (lane == 63 && wtot) wbase = atomicAdd(&s_cnt, wtot);
+    wbase = __shfl(wbase, 63, 64);
+    int slot = wbase + incl - mycnt;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (ok[j] && (uint64_t)vk[j] >= tge) {
+        if (slot < CAP) s_ck[slot] = comp_key(vk[j], (uint32_t)(e0 + j));
+        else bad = 1;  // cannot happen (see the checkpoint); kept as a guard
+        ++slot;
+      }
+
+    // checkpoint: the buffer holds at most kTopkMaxK + GROUP * CHUNK entries because it
+    // is cut back to K <= kTopkMaxK whenever fewer than GROUP * CHUNK slots remain
+    if ((ci + 1) % GROUP == 0 && ci + 1 < nchunks) {
+      __syncthreads();
+      const int n = min(s_cnt, CAP);
+      if (n > CAP - GROUP * CHUNK && n > K) {
+        radix_select<TB>(s_ck, n, K, s_hist, s_res, t);
+        const uint64_t P = s_res[0];
+        const int D = (int)s_res[1];
+        compact<TB, CAP>(s_ck, n, P, D, &s_cnt, t);
+        // later elements have larger indices than every buffered one, so with the
+        // value part of the threshold resolved a later element needs a larger value
+        if (D >= T::VB) tge = (P >> (D - T::VB)) + 1;
+        else tge = P << (T::VB - D);
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  // final selection: exactly K entries
+  int n = min(s_cnt, CAP);
+  if (n > K) {
+    radix_select<TB>(s_ck, n, K, s_hist, s_res, t);
+    n = compact<TB, CAP>(s_ck, n, s_res[0], (int)s_res[1], &s_cnt, t);
+  }
+  // logsumexp of the row
+  float M = m;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  double sl = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f((m - M) * kTkLog2e);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sl += __shfl_xor(sl, o, 64);
+  if (lane == 0) {
+    s_m[w] = M;
+    s_s[w] = sl;
+  }
+  const int anybad = __syncthreads_or(bad);
+  float Mb = s_m[0];
+  for (int i = 1; i < kTkThreads / 64; ++i) Mb = fmaxf(Mb, s_m[i]);
+  double Sd = 0.0;
+  for (int i = 0; i < kTkThreads / 64; ++i)
+    if (s_m[i] != -INFINITY) Sd += s_s[i] * (double)__builtin_amdgcn_exp2f((s_m[i] - Mb) * kTkLog2e);
+  const float Sb = (float)Sd;
+  if (t == 0 && (anybad || Mb == -INFINITY || n != K)) atomicOr(flags, 1);
+  if (t == 0 && lse_out) lse_out[row] = Mb + __builtin_amdgcn_logf(Sb) * kTkLn2;
+  // rank of each selected entry among the K (keys are unique), then write in order
+  const float invS = 1.f / Sb;
+  for (int i = t; i < n; i += kTkThreads) {
+    const uint64_t c = s_ck[i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) rank += s_ck[j] > c ? 1 : 0;
+    const uint32_t ix = ~(uint32_t)c;
+    const float xv = T::value((uint32_t)(c >> 32));
+    if (rank < K) {
+      idx_out[row * K + rank] = (int32_t)ix;
+      p_out[row * K + rank] = __builtin_amdgcn_exp2f((xv - Mb) * kTkLog2e) * invS;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_teacher_topk(int dtype, const void *logits, int64_t N, int64_t V, int32_t K,
+                               int32_t *idx, float *p, float *lse, int *flags, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int es = dtype == 1 ? 2 : 4;
+  const bool vec = ((uintptr_t)logits % 16 == 0) && ((V * es) % 16 == 0);
+  const dim3 grid((unsigned)N), block(kTkThreads);
+  if (dtype == 1) {
+    if (vec)
+      hipLaunchKernelGGL((k_teacher_topk<1, true>), grid, block, 0, s, logits, (long long)V, K,
+                         idx, p, lse, flags);
+    else
+      hipLaunchKernelGGL((k_teacher_topk<1, false>), grid, block, 0, s, logits, (long long)V, K,
+                         idx, p, lse, flags);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((k_teacher_topk<0, true>), grid, block, 0, s, logits, (long long)V, K,
+                         idx, p, lse, flags);
+    else
+      hipLaunchKernelGGL((k_teacher_topk<0, false>), grid, block, 0, s, logits, (long long)V, K,
+                         idx, p, lse, flags);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kd

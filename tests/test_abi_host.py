@@ -160,3 +160,42 @@ def test_forward_entry_rejects_bad_calls_on_host(lib, kw, code):
 def test_backward_entry_rejects_bad_calls_on_host(lib, kw, code):
     assert _call_bwd(lib, **kw) == code
     assert lib.kd_last_error()
+
+
+def _call_topk(lib, **kw):
+    base = dict(logits=0x100000, dtype=1, N=64, V=1000, K=100, idx=0x200000, p=0x300000,
+                lse=None, ws=0x400000, wsb=256, stream=None)
+    base.update(kw)
+    b = base
+    return lib.kd_teacher_topk(b["logits"], b["dtype"], b["N"], b["V"], b["K"], b["idx"], b["p"],
+                               b["lse"], b["ws"], b["wsb"], b["stream"])
+
+
+def test_topk_workspace_query(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.kd_topk_workspace_bytes(ctypes.byref(out)) == OK and out.value == 256
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=1001), E_ARG),            # K > V
+    (dict(K=0), E_ARG),
+    (dict(K=257), E_UNSUPPORTED),     # above the largest supported K
+    (dict(V=0), E_ARG),
+    (dict(N=-1), E_ARG),
+    (dict(dtype=5), E_ARG),
+    (dict(logits=None), E_ARG),
+    (dict(idx=None), E_ARG),
+    (dict(logits=0x100001), E_ARG),   # bf16 logits must be 2-byte aligned
+    (dict(p=0x300002), E_ARG),
+    (dict(ws=None), E_ARG),
+    (dict(ws=0x400010), E_ARG),
+    (dict(wsb=100), E_WORKSPACE),
+    (dict(V=1 << 31, K=10), E_UNSUPPORTED),
+])
+def test_topk_rejects_bad_calls_on_host(lib, kw, code):
+    assert _call_topk(lib, **kw) == code
+    assert lib.kd_last_error()
+
+
+def test_topk_with_no_rows_does_nothing(lib):
+    assert _call_topk(lib, N=0, logits=None, idx=None, p=None) == OK
