@@ -41,6 +41,9 @@ def parse():
                     help="time the forward half (kd_chunked_kl_fwd) and the backward half "
                          "(kd_chunked_kl_bwd) separately instead of the fused call; prints one "
                          "JSON line")
+    ap.add_argument("--topk", action="store_true",
+                    help="time the teacher top-K cache producer (kd_teacher_topk) on N=32768 rows "
+                         "of V=128256 bf16 teacher logits, K=100; prints one JSON line")
     ap.add_argument("--memory-sweep", action="store_true",
                     help="measure peak device memory of one call for N = 4K .. 256K tokens "
                          "(d=3072, V=128256, K=100, chunk 4096) and fit a + b*N; prints one "
@@ -51,9 +54,9 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=("kd_kernels.hip", "kd_api.hip", "kd_internal.h")):
     h = hashlib.sha256()
-    for f in ("kd_kernels.hip", "kd_api.hip", "kd_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "output_head_kl_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -89,6 +92,97 @@ def cpu_baseline(inp, rows):
     return {"value": len(sel) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(sel)} seeded token rows of the same workload (full V and d), "
                       f"float64 numpy, loss + dh + dW, {dt:.1f} s"}
+
+
+def topk_traffic(workload):
+    """HBM bytes per launch of the top-K kernel recorded under profiles/, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic_topk.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if (rec.get("source_hash") != kernel_source_hash(("kd_topk.hip", "kd_internal.h"))
+            or rec.get("workload") != workload):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def bench_topk(args):
+    """Teacher top-K cache producer: one row of logits per token, read once (HBM-bound)."""
+    import torch
+
+    import output_head_kl_amd as kd
+    import synth
+    N, V, K = args.N or 32768, 128256, 100
+    seed = synth.BASE_SEED + 10
+    t0 = time.perf_counter()
+    bits = synth.make_teacher_logits(N, V, seed=seed, threads=16)
+    print(f"[bench] generated teacher logits N={N} V={V} in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((N, K), dtype=torch.int32, device="cuda")
+    pr = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    lse = torch.empty(N, dtype=torch.float32, device="cuda")
+    lib = kd._lib()
+    strm = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        kd._check(lib.kd_teacher_topk(x.data_ptr(), kd.KD_BF16, N, V, K, idx.data_ptr(),
+                                      pr.data_ptr(), lse.data_ptr(), ws.data_ptr(), 256, strm))
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    kd.profile_read()
+    kd.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kd.profile_enable(False)
+    kt = _kernel_table(kd.profile_read(), args.steps)
+    ms = el / args.steps * 1e3
+    kern_ms = kt["teacher_topk"]["avg_ms"]
+    algo_bytes = N * V * 2 + N * K * 8 + N * 4       # logits once; idx, p and lse written
+    achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
+    workload = f"teacher_topk_N{N}_V{V}_K{K}_bf16"
+    res = {
+        "metric": "tokens/s, teacher top-K cache producer (top-100 probabilities per position)",
+        "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": workload, "N": N, "V": V, "K": K},
+        "roofline": {"bound": "hbm", "kernel": "teacher_topk", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": topk_traffic(workload)},
+        "kernels": kt, "cpu_baseline": None,
+    }
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * 2**30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if not args.no_cpu_baseline:
+        from oracle.topk import topk_probs
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count()
+        rows = args.cpu_rows
+        sub = synth.bf16_bits_to_f32(bits[:rows]).astype(np.float64)
+        t0 = time.perf_counter()
+        topk_probs(sub, K)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": rows / dt, "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"the first {rows} rows of the same logits, float64 numpy "
+                                         f"(full-row stable sort), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
 
 
 def memory_sweep():
@@ -213,6 +307,12 @@ def main():
     args = parse()
     if args.memory_sweep:
         memory_sweep()
+        return
+    if args.topk:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_topk(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "

@@ -165,7 +165,7 @@ int kd_chunked_kl_bwd(const void *h, const void *W, int32_t dtype,
  *   logits   [N, V]  dtype (KD_BF16 or KD_F32), aligned to its element size
  *   topk_idx [N, K]  int32;  topk_p [N, K] float32;  row_lse [N] float32 or NULL
  *   workspace        >= kd_topk_workspace_bytes() bytes, 256-byte aligned
- * Sizes: N >= 0, 1 <= K <= min(V, 256), V < 2^31, N < 2^31.
+ * Sizes: N >= 0, 1 <= K <= min(V, 256), V < 2^29, N < 2^31.
  * Each row is read from device memory once.  The call synchronises the stream once,
  * at the end, to read the validity flag: a row with a NaN or +inf logit, or with no
  * finite logit, gives KD_E_INDEX and the outputs are undefined.  Other errors are

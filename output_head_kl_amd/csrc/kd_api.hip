@@ -345,8 +345,8 @@ int kd_teacher_topk(const void *logits, int32_t dtype, int64_t N, int64_t V, int
   if (N < 0 || V < 1 || K < 1) return fail(KD_E_ARG, "need N >= 0, V >= 1, K >= 1");
   if (K > V) return fail(KD_E_ARG, "K = %d exceeds V = %lld", K, (long long)V);
   if (K > kd::kTopkMaxK) return fail(KD_E_UNSUPPORTED, "K = %d above %d", K, kd::kTopkMaxK);
-  if (V >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
-    return fail(KD_E_UNSUPPORTED, "V and N must be below 2^31");
+  if (V >= ((int64_t)1 << 29) || N >= ((int64_t)1 << 31))
+    return fail(KD_E_UNSUPPORTED, "V must be below 2^29 and N below 2^31");
   if (N > 0 && (!logits || !topk_idx || !topk_p)) return fail(KD_E_ARG, "logits, topk_idx and topk_p are required");
   if (!workspace) return fail(KD_E_ARG, "workspace is required");
   const size_t es = dtype == KD_BF16 ? 2 : 4;

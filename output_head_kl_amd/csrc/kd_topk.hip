@@ -28,6 +28,15 @@ constexpr float kTkLog2e = 1.4426950408889634f;
 constexpr float kTkLn2 = 0.6931471805599453f;
 constexpr int kTkThreads = 256;
 
+// Workgroup barrier that orders LDS accesses only: every exchange between threads in
+// this kernel goes through LDS, and a full __syncthreads would also wait for the
+// global loads in flight (the prefetch ring).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Order-preserving 32-bit key of a float (larger float -> larger key); -0.0 is +0.0.
 __device__ __forceinline__ uint32_t f_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -43,17 +52,11 @@ template <> struct TkT<1> {  // bf16 logits: 16-bit value keys, 8 elements per l
     const uint32_t u = (k & 0x8000u) ? ((k & 0x7FFFu) << 16) : ((~k & 0xFFFFu) << 16);
     return __uint_as_float(u);
   }
-  static __device__ __forceinline__ float load1(const void *p, long long i) {
-    return __uint_as_float((uint32_t)((const unsigned short *)p)[i] << 16);
-  }
-  static __device__ __forceinline__ void load_vec(const void *p, long long i, float (&x)[8]) {
-    const uint4 v = *(const uint4 *)((const unsigned short *)p + i);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = __uint_as_float(w[j] << 16);
-      x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
+  // the float x with "x >= result" <=> "vkey(x) >= k" for every non-NaN x
+  static __device__ __forceinline__ float threshold(uint64_t k) {
+    if (k <= 0x007Fu) return -INFINITY;     // at or below the key of -inf
+    if (k >= 0xFF80u) return INFINITY;      // at or above the key of +inf
+    return value((uint32_t)k);
   }
 };
 template <> struct TkT<0> {  // fp32 logits: 32-bit value keys, 4 elements per load
@@ -62,12 +65,10 @@ template <> struct TkT<0> {  // fp32 logits: 32-bit value keys, 4 elements per l
   static __device__ __forceinline__ float value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
   }
-  static __device__ __forceinline__ float load1(const void *p, long long i) {
-    return ((const float *)p)[i];
-  }
-  static __device__ __forceinline__ void load_vec(const void *p, long long i, float (&x)[4]) {
-    const float4 v = *(const float4 *)((const float *)p + i);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  static __device__ __forceinline__ float threshold(uint64_t k) {
+    if (k <= 0x007FFFFFu) return -INFINITY;
+    if (k >= 0xFF800000u) return INFINITY;
+    return value((uint32_t)k);
   }
 };
 
@@ -88,7 +89,7 @@ __device__ void radix_select(const uint64_t *s_ck, int n, int need, uint32_t *s_
   for (int level = 0; level < TB / 8; ++level) {
     const int shift = TB - 8 * (level + 1);
     s_hist[t] = 0u;
-    __syncthreads();
+    lds_sync();
     // entries whose digits above this level equal the prefix (at the first level of a
     // 64-bit key every entry matches: a shift by 64 would be undefined)
     const bool all = shift + 8 >= 64;
@@ -96,7 +97,7 @@ __device__ void radix_select(const uint64_t *s_ck, int n, int need, uint32_t *s_
       const uint64_t c = s_ck[i];
       if (all || (c >> (shift + 8)) == P) atomicAdd(&s_hist[(c >> shift) & 255u], 1u);
     }
-    __syncthreads();
+    lds_sync();
     // suffix sums over the 256 bins: wave w holds bins 64w..64w+63
     const int lane = t & 63, w = t >> 6;
     const uint32_t h = s_hist[t];
@@ -108,7 +109,7 @@ __device__ void radix_select(const uint64_t *s_ck, int n, int need, uint32_t *s_
     }
     __shared__ uint32_t s_wtot[4];
     if (lane == 0) s_wtot[w] = sfx;
-    __syncthreads();
+    lds_sync();
     uint32_t later = 0;
     for (int w2 = w + 1; w2 < 4; ++w2) later += s_wtot[w2];
     const uint32_t S = sfx + later;  // entries of this prefix with digit >= t
@@ -117,19 +118,19 @@ __device__ void radix_select(const uint64_t *s_ck, int n, int need, uint32_t *s_
       s_above = (int)(S - h);
       s_inbin = (int)h;
     }
-    __syncthreads();
+    lds_sync();
     const int bin = s_bin, above = s_above, inbin = s_inbin;
     need -= above;
     P = (P << 8) | (uint64_t)bin;
     D += 8;
-    __syncthreads();  // s_bin and friends are rewritten by the next level
+    lds_sync();  // s_bin and friends are rewritten by the next level
     if (inbin == need) break;
   }
   if (t == 0) {
     s_res[0] = P;
     s_res[1] = (uint64_t)D;
   }
-  __syncthreads();
+  lds_sync();
 }
 
 // Keeps the entries selected by (P, D) at the front of the buffer (order arbitrary).
@@ -148,14 +149,14 @@ __device__ int compact(uint64_t *s_ck, int n, uint64_t P, int D, int *s_cnt, int
     sel[r] = i < n && (mine[r] >> (TB - D)) >= P;
     nm += sel[r] ? 1 : 0;
   }
-  __syncthreads();
+  lds_sync();
   if (t == 0) *s_cnt = 0;
-  __syncthreads();
+  lds_sync();
   int slot = nm ? atomicAdd(s_cnt, nm) : 0;
 #pragma unroll
   for (int r = 0; r < PER; ++r)
     if (sel[r]) s_ck[slot++] = mine[r];
-  __syncthreads();
+  lds_sync();
   return *s_cnt;
 }
 
@@ -181,78 +182,118 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
   const long long row = blockIdx.x;
   const char *rp = (const char *)logits + row * V * (DT == 1 ? 2 : 4);
   if (t == 0) s_cnt = 0;
-  __syncthreads();
+  lds_sync();
 
-  uint64_t tge = 0;  // candidate iff value key >= tge (tge may be 2^VB: nothing passes)
+  // Candidate test: x >= tf, a float threshold equivalent to "value key >= tge" (the key
+  // order is the float order, +0.0 and -0.0 alike); -inf lets everything through.
+  uint64_t tge = 0;
+  float tf = -INFINITY;
   // running max and sum of exp(x - max) per lane; the sum is kept in float64 (a row
-  // has ~V/256 terms per lane), each term is a float32 exp2
+  // has ~V/256 terms per lane), each term is a float32 exp2.  A NaN or +inf logit
+  // makes the final sum NaN or the maximum +inf, which is how bad rows are found.
   float m = -INFINITY;
   double s = 0.0;
   int bad = 0;
-  const long long nchunks = (V + CHUNK - 1) / CHUNK;
-  for (long long ci = 0; ci < nchunks; ++ci) {
-    const long long e0 = ci * CHUNK + (long long)t * EPL;
-    float x[EPL];
-    bool ok[EPL];
-    if (VEC && e0 + EPL <= V) {
-      if constexpr (VEC) T::load_vec(rp, e0, x);
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) ok[j] = true;
+  const int nchunks = (int)((V + CHUNK - 1) / CHUNK);
+  const int Vi = (int)V;
+  // Raw 16-byte (or one-element) loads run PF chunks ahead of their use, so that a
+  // row's chunks are not each a full memory round trip.  Buffer loads with the row as
+  // the resource's range: offsets past the row read zero without a branch (a load
+  // under a branch would make the compiler wait for it at the join).
+  constexpr int PF = 4;
+  constexpr int ES = DT == 1 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)rp, (short)0, Vi * ES, 0x00020000);
+  auto load_raw = [&](int ci) {
+    uint4 r = {0u, 0u, 0u, 0u};
+    const int e0 = ci * CHUNK + t * EPL;
+    const int o = e0 < Vi ? e0 * ES : (int)0x7FFFFFFF;   // past the row: reads zero
+    if constexpr (VEC) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
+      r = uint4{v[0], v[1], v[2], v[3]};
+    } else if constexpr (DT == 1) {
+      r.x = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, o, 0, 0);
     } else {
+      r.x = __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0);
+    }
+    return r;
+  };
+  uint4 ring[PF];
+  // issued in slot order (the loop waits for them in that order)
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    ring[u] = load_raw(u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // The trip count is a whole number of ring turns (chunks past the row read nothing
+  // and add nothing), so each slot keeps its registers: a slot is decoded, then
+  // reloaded in place, and only its own load is waited for.
+  const int nch_pad = (nchunks + PF - 1) / PF * PF;
+  for (int c0 = 0; c0 < nch_pad; c0 += PF)
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    const int ci = c0 + u;
+    const int e0 = ci * CHUNK + t * EPL;
+    // all EPL elements of a lane are in the row or none is (V % EPL == 0 when VEC)
+    const bool in = e0 < Vi;
+    float x[EPL];
+    {
+      const uint32_t wd[4] = {ring[u].x, ring[u].y, ring[u].z, ring[u].w};
 #pragma unroll
       for (int j = 0; j < EPL; ++j) {
-        ok[j] = e0 + j < V;
-        x[j] = ok[j] ? T::load1(rp, e0 + j) : -INFINITY;
+        uint32_t b;
+        if (DT == 1) b = VEC ? ((j & 1) ? (wd[j >> 1] & 0xFFFF0000u) : (wd[j >> 1] << 16))
+                             : (wd[0] << 16);
+        else b = VEC ? wd[j] : wd[0];
+        x[j] = in ? __uint_as_float(b) : -INFINITY;
       }
     }
-    // online logsumexp of this lane; NaN and +inf are errors
-    float lm = -INFINITY;
+    ring[u] = load_raw(ci + PF);
+    // online logsumexp of this lane
+    float lm = x[0];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      bad |= (x[j] != x[j]) | (x[j] == INFINITY);
-      lm = fmaxf(lm, x[j]);
-    }
+    for (int j = 1; j < EPL; ++j) lm = fmaxf(lm, x[j]);
     if (lm > m) {
       s = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f((m - lm) * kTkLog2e);
       m = lm;
     }
     if (m != -INFINITY) {
+      // (x - m) first: the difference of two logits is exact or nearly so, while
+      // x * log2(e) - m * log2(e) would lose |m| * 2^-24 to the rounding of m * log2(e)
       float part = 0.f;  // at most 8 terms in float32
 #pragma unroll
       for (int j = 0; j < EPL; ++j) part += __builtin_amdgcn_exp2f((x[j] - m) * kTkLog2e);
       s += (double)part;
     }
-    // candidates: one LDS atomic per wave
-    uint32_t vk[EPL];
+    // candidates (rare once the threshold has risen): skipped when no lane has one
     int mycnt = 0;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      vk[j] = T::vkey(x[j]);
-      mycnt += (ok[j] && (uint64_t)vk[j] >= tge) ? 1 : 0;
-    }
-    int incl = mycnt;  // inclusive prefix over the wave
+    for (int j = 0; j < EPL; ++j) mycnt += (in && x[j] >= tf) ? 1 : 0;
+    if (__ballot(mycnt > 0)) {
+      int incl = mycnt;  // inclusive prefix over the wave
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    const int wtot = __shfl(incl, 63, 64);
-    int wbase = 0;
-    if (lane == 63 && wtot) wbase = atomicAdd(&s_cnt, wtot);
-    wbase = __shfl(wbase, 63, 64);
-    int slot = wbase + incl - mycnt;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (ok[j] && (uint64_t)vk[j] >= tge) {
-        if (slot < CAP) s_ck[slot] = comp_key(vk[j], (uint32_t)(e0 + j));
-        else bad = 1;  // cannot happen (see the checkpoint); kept as a guard
-        ++slot;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
       }
+      const int wtot = __shfl(incl, 63, 64);
+      int wbase = 0;
+      if (lane == 63) wbase = atomicAdd(&s_cnt, wtot);
+      wbase = __shfl(wbase, 63, 64);
+      int slot = wbase + incl - mycnt;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (in && x[j] >= tf) {
+          if (slot < CAP) s_ck[slot] = comp_key(T::vkey(x[j]), (uint32_t)(e0 + j));
+          else bad = 1;  // cannot happen (see the checkpoint); kept as a guard
+          ++slot;
+        }
+    }
 
     // checkpoint: the buffer holds at most kTopkMaxK + GROUP * CHUNK entries because it
     // is cut back to K <= kTopkMaxK whenever fewer than GROUP * CHUNK slots remain
     if ((ci + 1) % GROUP == 0 && ci + 1 < nchunks) {
-      __syncthreads();
+      lds_sync();
       const int n = min(s_cnt, CAP);
       if (n > CAP - GROUP * CHUNK && n > K) {
         radix_select<TB>(s_ck, n, K, s_hist, s_res, t);
@@ -263,11 +304,12 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
         // value part of the threshold resolved a later element needs a larger value
         if (D >= T::VB) tge = (P >> (D - T::VB)) + 1;
         else tge = P << (T::VB - D);
+        tf = T::threshold(tge);
       }
-      __syncthreads();
+      lds_sync();
     }
   }
-  __syncthreads();
+  lds_sync();
   // final selection: exactly K entries
   int n = min(s_cnt, CAP);
   if (n > K) {
@@ -292,7 +334,8 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
   for (int i = 0; i < kTkThreads / 64; ++i)
     if (s_m[i] != -INFINITY) Sd += s_s[i] * (double)__builtin_amdgcn_exp2f((s_m[i] - Mb) * kTkLog2e);
   const float Sb = (float)Sd;
-  if (t == 0 && (anybad || Mb == -INFINITY || n != K)) atomicOr(flags, 1);
+  const bool finite = Mb > -INFINITY && Mb < INFINITY && Sd == Sd && Sd < (double)INFINITY;
+  if (t == 0 && (anybad || !finite || n != K)) atomicOr(flags, 1);
   if (t == 0 && lse_out) lse_out[row] = Mb + __builtin_amdgcn_logf(Sb) * kTkLn2;
   // rank of each selected entry among the K (keys are unique), then write in order
   const float invS = 1.f / Sb;

@@ -190,7 +190,7 @@ def test_topk_workspace_query(lib):
     (dict(ws=None), E_ARG),
     (dict(ws=0x400010), E_ARG),
     (dict(wsb=100), E_WORKSPACE),
-    (dict(V=1 << 31, K=10), E_UNSUPPORTED),
+    (dict(V=1 << 29, K=10), E_UNSUPPORTED),
 ])
 def test_topk_rejects_bad_calls_on_host(lib, kw, code):
     assert _call_topk(lib, **kw) == code
