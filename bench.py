@@ -41,6 +41,9 @@ def parse():
                     help="time the forward half (kd_chunked_kl_fwd) and the backward half "
                          "(kd_chunked_kl_bwd) separately instead of the fused call; prints one "
                          "JSON line")
+    ap.add_argument("--shard", type=int, default=0,
+                    help="time one GPU's share of a vocabulary-sharded head: rows [0, V/G) of W "
+                         "with the full token batch (forward statistics + backward); G = value")
     ap.add_argument("--topk", action="store_true",
                     help="time the teacher top-K cache producer (kd_teacher_topk) on N=32768 rows "
                          "of V=128256 bf16 teacher logits, K=100; prints one JSON line")
@@ -303,6 +306,57 @@ def bench_split(args, kd, torch, cfg, h, W, idx, p, mask, ws):
     print(json.dumps(res), flush=True)
 
 
+def bench_shard(args, kd, torch, cfg, h, W, idx, p, mask):
+    """One vocabulary shard (rows [0, V/G) of W) over the whole token batch: the forward
+    statistics and the backward, as one GPU of a G-way tensor-parallel head would run
+    between its collectives (which are not part of this)."""
+    G = args.shard
+    Vs = (cfg.V + G - 1) // G
+    Ws = W[:Vs].contiguous()
+    ws = torch.empty(kd.workspace_bytes(cfg.N, cfg.d, Vs, cfg.K, cfg.chunk,
+                                        kd.KD_BF16 if cfg.dtype == "bf16" else kd.KD_F32),
+                     dtype=torch.uint8, device="cuda")
+    lse = torch.full((cfg.N,), 14.0, dtype=torch.float32, device="cuda")   # stands in for the
+    g = torch.ones(1, dtype=torch.float32, device="cuda")                  # combined logsumexp
+
+    def step():
+        kd.vocab_shard_fwd(h, Ws, idx, p, 0, cfg.V, chunk=cfg.chunk, workspace=ws)
+        kd.vocab_shard_bwd(h, Ws, idx, p, lse, 0, cfg.V, g, mask, chunk=cfg.chunk, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kd.profile_read()
+    kd.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kd.profile_enable(False)
+    kt = _kernel_table(kd.profile_read(), args.steps)
+    ms = el / args.steps * 1e3
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    gem = {k: v for k, v in kt.items() if k in GEMM_CLASSES}
+    dom = max(gem, key=lambda k: gem[k]["total_ms_per_step"])
+    achieved = 2.0 * cfg.N * Vs * cfg.d / gem[dom]["launches_per_step"] / (gem[dom]["avg_ms"] * 1e-3) / 1e12
+    res = {
+        "metric": f"tokens/s of one GPU's share of a {G}-way vocabulary-sharded head "
+                  f"(forward statistics + backward, collectives excluded)",
+        "value": round(cfg.N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"vocab_shard_{G}_N{cfg.N}_d{cfg.d}_Vshard{Vs}_K{cfg.K}_chunk{cfg.chunk}_{cfg.dtype}",
+                   "N": cfg.N, "d": cfg.d, "V": cfg.V, "V_shard": Vs, "K": cfg.K, "chunk": cfg.chunk},
+        "tflops_8NVsd": round(8.0 * cfg.N * Vs * cfg.d / (ms * 1e-3) / 1e12, 1),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+        "kernels": kt, "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.memory_sweep:
@@ -349,6 +403,8 @@ def main():
 
     if args.split:
         return bench_split(args, kd, torch, cfg, h, W, idx, p, mask, ws)
+    if args.shard:
+        return bench_shard(args, kd, torch, cfg, h, W, idx, p, mask)
 
     for _ in range(args.warmup):
         out = step()

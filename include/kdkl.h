@@ -150,6 +150,59 @@ int kd_chunked_kl_bwd(const void *h, const void *W, int32_t dtype,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Vocabulary shards -- one GPU's share of an output head split over the vocabulary.
+ *
+ * The pages' implementation takes tensor-parallel rank and size arguments
+ * (codewithpapers.app record of the released code: tensor_parallel_rank,
+ * tensor_parallel_size); here a shard is W_shard = rows [v_offset, v_offset + V_shard)
+ * of a V_total-row W, teacher indices stay global (entries outside the shard are
+ * skipped), and the three calls below are what one GPU runs between the collectives:
+ *
+ * kd_vocab_shard_fwd: per token n, over the shard's logits z[n,v] (v in the shard)
+ *   shard_max[n]    = max_v z[n,v]
+ *   shard_sumexp[n] = sum_v exp(z[n,v] - shard_max[n])
+ *   shard_pz[n]     = sum_{k: idx[n,k] in the shard} p[n,k] * z[n,idx[n,k]]
+ *   zg [N,K]        = optional: z at the in-shard entries, 0 elsewhere (NULL = skip)
+ *   (these three [N] float32 arrays are what the shards exchange: an all-gather)
+ * kd_vocab_shard_combine: from G shards' statistics laid out [G][N] each,
+ *   row_lse[n] = M + log sum_g shard_sumexp[g,n] exp(shard_max[g,n] - M), M = max_g,
+ *   l[n] = sum_k p log p - sum_g shard_pz[g,n] + (sum_k p) row_lse[n],
+ *   loss = sum_n mask[n] l[n] / count; row_loss[n] = mask[n] ? l[n] : 0 (optional).
+ *   Workspace: kd_vocab_shard_combine_workspace_bytes(N).  One stream synchronisation.
+ * kd_vocab_shard_bwd: with the global row_lse and the upstream gradient g
+ *   (grad_loss[0], on the device), for v in the shard
+ *   dz[n,v] = g (mask[n]/count) (M[n] exp(z[n,v] - row_lse[n]) - sum_{k: idx=v} p[n,k]),
+ *   dh_partial [N,d] float32 = dz @ W_shard  (the shards' partials are summed: an
+ *                              all-reduce; then rounded to dtype by the caller),
+ *   dW_shard [V_shard,d] float32 = dz^T @ h  (overwritten).
+ * Sizes, dtypes, alignment, workspace (kd_workspace_bytes with V = V_shard), stream
+ * behaviour and errors as kd_chunked_kl_fwd_bwd; teacher indices are checked against
+ * [0, V_total) and v_offset + V_shard <= V_total <= 2^24.  With G = 1 and the whole
+ * vocabulary as the shard, the three calls give the loss, dh and dW of
+ * kd_chunked_kl_fwd_bwd up to float rounding.
+ */
+int kd_vocab_shard_fwd(const void *h, const void *W_shard, int32_t dtype,
+                       const int32_t *topk_idx, const float *topk_p,
+                       int64_t N, int64_t d, int64_t V_shard, int64_t v_offset,
+                       int64_t V_total, int32_t K, int64_t chunk,
+                       float *shard_max, float *shard_sumexp, float *shard_pz, float *zg,
+                       void *workspace, size_t workspace_bytes, void *stream);
+int kd_vocab_shard_combine_workspace_bytes(int64_t N, size_t *bytes_out);
+int kd_vocab_shard_combine(const float *shard_max, const float *shard_sumexp,
+                           const float *shard_pz, int32_t G, const float *topk_p,
+                           const uint8_t *loss_mask, int64_t N, int32_t K, float *loss,
+                           float *row_lse, float *row_loss,
+                           void *workspace, size_t workspace_bytes, void *stream);
+int kd_vocab_shard_bwd(const void *h, const void *W_shard, int32_t dtype,
+                       const int32_t *topk_idx, const float *topk_p,
+                       const uint8_t *loss_mask,
+                       int64_t N, int64_t d, int64_t V_shard, int64_t v_offset,
+                       int64_t V_total, int32_t K, int64_t chunk,
+                       const float *row_lse, const float *grad_loss,
+                       float *dh_partial, float *dW_shard,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kd_teacher_topk -- the teacher top-K cache producer.
  *
  * The offline step that runs the teacher once and keeps, per position, its most

@@ -13,7 +13,8 @@ import os
 from typing import Optional
 
 __all__ = ["KDError", "library_path", "workspace_bytes", "fwd_bwd", "fwd", "bwd",
-           "chunked_kl_loss", "teacher_topk", "profile_enable", "profile_read", "profile_classes", "KD_F32",
+           "chunked_kl_loss", "teacher_topk", "vocab_shard_fwd", "vocab_shard_combine",
+           "vocab_shard_bwd", "profile_enable", "profile_read", "profile_classes", "KD_F32",
            "KD_BF16"]
 
 KD_F32, KD_BF16 = 0, 1
@@ -54,6 +55,17 @@ def _lib():
     lib.kd_chunked_kl_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
                                       vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_bwd.restype = ctypes.c_int
+    lib.kd_vocab_shard_fwd.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, i64, i64, i32, i64,
+                                       vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_vocab_shard_fwd.restype = ctypes.c_int
+    lib.kd_vocab_shard_combine_workspace_bytes.argtypes = [i64, ctypes.POINTER(sz)]
+    lib.kd_vocab_shard_combine_workspace_bytes.restype = ctypes.c_int
+    lib.kd_vocab_shard_combine.argtypes = [vp, vp, vp, i32, vp, vp, i64, i32, vp, vp, vp, vp, sz,
+                                           vp]
+    lib.kd_vocab_shard_combine.restype = ctypes.c_int
+    lib.kd_vocab_shard_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i64, i32,
+                                       i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_vocab_shard_bwd.restype = ctypes.c_int
     lib.kd_topk_workspace_bytes.argtypes = [ctypes.POINTER(sz)]
     lib.kd_topk_workspace_bytes.restype = ctypes.c_int
     lib.kd_teacher_topk.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, sz, vp]
@@ -271,6 +283,70 @@ def teacher_topk(logits, K: int = 100, lse: bool = True, workspace=None, stream=
     _check(_lib().kd_teacher_topk(_ptr(logits), dt, N, V, K, _ptr(idx), _ptr(p), _ptr(row_lse),
                                   _ptr(workspace), workspace.numel(), _stream(stream, dev)))
     return (idx, p, row_lse) if lse else (idx, p)
+
+
+def vocab_shard_fwd(h, W_shard, topk_idx, topk_p, v_offset: int, V_total: int,
+                    chunk: int = 2048, zg: bool = False, workspace=None, stream=None):
+    """One vocabulary shard's forward statistics: ``(shard_max, shard_sumexp, shard_pz)``
+    [N] float32 each (and zg [N, K] with ``zg``)."""
+    import torch
+    dt, N, d, Vs, K, _ = _prep(h, W_shard, topk_idx, topk_p, None)
+    dev = h.device
+    workspace = _workspace(workspace, N, d, Vs, K, chunk, dt, dev)
+    st = [torch.empty(N, dtype=torch.float32, device=dev) for _ in range(3)]
+    zgt = torch.empty((N, K), dtype=torch.float32, device=dev) if zg else None
+    _check(_lib().kd_vocab_shard_fwd(
+        _ptr(h), _ptr(W_shard), dt, _ptr(topk_idx), _ptr(topk_p), N, d, Vs, v_offset, V_total, K,
+        chunk, _ptr(st[0]), _ptr(st[1]), _ptr(st[2]), _ptr(zgt), _ptr(workspace),
+        workspace.numel(), _stream(stream, h.device)))
+    return (*st, zgt) if zg else tuple(st)
+
+
+def vocab_shard_combine(shard_max, shard_sumexp, shard_pz, topk_p, loss_mask=None,
+                        workspace=None, stream=None):
+    """Global ``(loss[1], row_lse [N], row_loss [N])`` from G shards' statistics, each
+    given as a [G, N] float32 tensor."""
+    import torch
+    G, N = shard_max.shape
+    K = topk_p.shape[1]
+    dev = shard_max.device
+    for t in (shard_max, shard_sumexp, shard_pz, topk_p):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("shard statistics and topk_p must be contiguous float32")
+    if loss_mask is not None and loss_mask.dtype == torch.bool:
+        loss_mask = loss_mask.view(torch.uint8)
+    if workspace is None:
+        out = ctypes.c_size_t(0)
+        _check(_lib().kd_vocab_shard_combine_workspace_bytes(N, ctypes.byref(out)))
+        workspace = torch.empty(int(out.value), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    row_lse = torch.empty(N, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(N, dtype=torch.float32, device=dev)
+    _check(_lib().kd_vocab_shard_combine(
+        _ptr(shard_max), _ptr(shard_sumexp), _ptr(shard_pz), G, _ptr(topk_p), _ptr(loss_mask), N,
+        K, _ptr(loss), _ptr(row_lse), _ptr(row_loss), _ptr(workspace), workspace.numel(),
+        _stream(stream, dev)))
+    return loss, row_lse, row_loss
+
+
+def vocab_shard_bwd(h, W_shard, topk_idx, topk_p, row_lse, v_offset: int, V_total: int,
+                    grad_loss=None, loss_mask=None, chunk: int = 2048, workspace=None,
+                    stream=None):
+    """One shard's ``(dh_partial [N, d] float32, dW_shard [V_shard, d] float32)``."""
+    import torch
+    dt, N, d, Vs, K, loss_mask = _prep(h, W_shard, topk_idx, topk_p, loss_mask)
+    dev = h.device
+    if grad_loss is None:
+        grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
+    grad_loss = grad_loss.reshape(1).contiguous()
+    workspace = _workspace(workspace, N, d, Vs, K, chunk, dt, dev)
+    dh = torch.empty((N, d), dtype=torch.float32, device=dev)
+    dW = torch.empty((Vs, d), dtype=torch.float32, device=dev)
+    _check(_lib().kd_vocab_shard_bwd(
+        _ptr(h), _ptr(W_shard), dt, _ptr(topk_idx), _ptr(topk_p), _ptr(loss_mask), N, d, Vs,
+        v_offset, V_total, K, chunk, _ptr(row_lse), _ptr(grad_loss), _ptr(dh), _ptr(dW),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return dh, dW
 
 
 def profile_enable(on: bool = True) -> None:

@@ -135,6 +135,7 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->off_boff = take((size_t)(L->nkeys + 1) * 4);
   L->off_bent = take((size_t)L->C_alloc * K * 4);
   L->off_wt = take(dtype == KD_BF16 ? (size_t)L->V_pad * d * 2 : 0);
+  L->off_idxloc = take((size_t)L->C_alloc * K * 4);
   L->total = off;
   return true;
 }
@@ -166,27 +167,47 @@ namespace {
 // The three entry points share one routine.  FUSED: loss, dh, dW.  FWD: loss and the
 // per-token logsumexp (saved for BWD).  BWD: dh and dW from the saved logsumexp and an
 // upstream gradient g of the loss, with the logits recomputed chunk by chunk.
-enum Mode { M_FUSED, M_FWD, M_BWD };
+// Vocabulary shards (one GPU's share of a tensor-parallel head, W = rows [v0, v0+V) of a
+// V_total vocabulary): SFWD exports per-token (max, sum exp, sum p*z) of the shard;
+// SBWD writes the shard's float32 dh partial and its dW rows, given the global lse.
+enum Mode { M_FUSED, M_FWD, M_BWD, M_SFWD, M_SBWD };
+
+struct ShardArgs {
+  int64_t v0 = 0, V_total = 0;
+  float *st_m = nullptr, *st_s = nullptr, *st_pz = nullptr;
+};
 
 int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *topk_idx,
         const float *topk_p, const uint8_t *loss_mask, int64_t N, int64_t d, int64_t V, int32_t K,
         int64_t chunk, float *loss, void *dh, float *dW, float *row_loss, float *row_lse,
         float *zg, const float *lse_in, const float *grad_loss, void *workspace,
-        size_t workspace_bytes, void *stream_v) {
+        size_t workspace_bytes, void *stream_v, const ShardArgs &sh = ShardArgs()) {
   g_err[0] = 0;
   int rc = check_sizes(N, d, V, K, chunk, dtype);
   if (rc != KD_OK) return rc;
-  const bool fwd = mode != M_BWD, bwd = mode != M_FWD;
+  const bool shard = mode == M_SFWD || mode == M_SBWD;
+  const bool fwd = mode == M_FUSED || mode == M_FWD || mode == M_SFWD;
+  const bool bwd = mode == M_FUSED || mode == M_BWD || mode == M_SBWD;
+  const int64_t V_idx = shard ? sh.V_total : V;  // range of the teacher indices
+  if (shard) {
+    if (sh.v0 < 0 || sh.V_total < V || sh.v0 > sh.V_total - V || sh.V_total > ((int64_t)1 << 24))
+      return fail(KD_E_ARG, "shard [%lld, %lld) does not lie in a vocabulary of %lld",
+                  (long long)sh.v0, (long long)(sh.v0 + V), (long long)sh.V_total);
+    if (mode == M_SFWD && N > 0 && (!sh.st_m || !sh.st_s || !sh.st_pz))
+      return fail(KD_E_ARG, "shard statistics outputs are required");
+  }
   if (!W || !workspace) return fail(KD_E_ARG, "W and workspace are required");
-  if (fwd && !loss) return fail(KD_E_ARG, "loss is required");
+  if (fwd && !shard && !loss) return fail(KD_E_ARG, "loss is required");
   if (bwd && !dW) return fail(KD_E_ARG, "dW is required");
-  if (mode == M_BWD && !grad_loss) return fail(KD_E_ARG, "grad_loss is required");
+  if ((mode == M_BWD || mode == M_SBWD) && !grad_loss)
+    return fail(KD_E_ARG, "grad_loss is required");
   if (N > 0 && (!h || !topk_idx || !topk_p))
     return fail(KD_E_ARG, "h, topk_idx and topk_p are required when N > 0");
   if (N > 0 && bwd && !dh) return fail(KD_E_ARG, "dh is required when N > 0");
   if (N > 0 && mode == M_FWD && !row_lse)
     return fail(KD_E_ARG, "row_lse is required (it is the state the backward call reads)");
-  if (N > 0 && mode == M_BWD && !lse_in) return fail(KD_E_ARG, "row_lse is required when N > 0");
+  if (N > 0 && (mode == M_BWD || mode == M_SBWD) && !lse_in)
+    return fail(KD_E_ARG, "row_lse is required when N > 0");
   auto mis = [](const void *p, uintptr_t a) { return p && ((uintptr_t)p % a) != 0; };
   if (mis(h, 16) || mis(W, 16) || mis(dh, 16) || mis(dW, 16))
     return fail(KD_E_ARG, "h, W, dh and dW must be 16-byte aligned");
@@ -216,10 +237,12 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
   int *bcursor = (int *)(ws + L.off_bcursor);
   int *boff = (int *)(ws + L.off_boff);
   unsigned *bent = (unsigned *)(ws + L.off_bent);
+  int32_t *idxloc = (int32_t *)(ws + L.off_idxloc);
   const int64_t es = dtype == KD_BF16 ? 2 : 4;
+  const int64_t es_dh = mode == M_SBWD ? 4 : es;  // a shard's dh partial stays float32
 
   if (N == 0) {
-    if (fwd) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
+    if (fwd && !shard) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
     if (bwd) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dW, (size_t)V * d * 4, stream));
     return KD_OK;
   }
@@ -227,7 +250,8 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
   // Validate the teacher entries and count the mask; the only host synchronisation.
   LAUNCH(kd::KC_MISC, kd::launch_fill_zero(ws + L.off_flags, L.off_acc - L.off_flags + 64, stream));
   LAUNCH(kd::KC_VALIDATE,
-         kd::launch_validate(topk_idx, topk_p, N * (int64_t)K, V, loss_mask, N, flags, dcount, stream));
+         kd::launch_validate(topk_idx, topk_p, N * (int64_t)K, V_idx, loss_mask, N, flags, dcount,
+                             stream));
   struct {
     int flags[2];
     unsigned long long count;
@@ -236,17 +260,17 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
   HIPCHK(hipStreamSynchronize(stream));
   if (hostv.flags[0])
     return fail(KD_E_INDEX, "a teacher index is outside [0, %lld) or a probability is negative or not finite",
-                (long long)V);
+                (long long)V_idx);
   const int64_t count = loss_mask ? (int64_t)hostv.count : N;
   const bool want_rows = row_loss || row_lse || zg;
 
   if (count == 0) {
-    if (fwd) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
+    if (fwd && !shard) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
     if (bwd) {
       LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dW, (size_t)V * d * 4, stream));
-      LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dh, (size_t)N * d * es, stream));
+      LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dh, (size_t)N * d * es_dh, stream));
     }
-    if (!fwd || !want_rows) return KD_OK;
+    if (!fwd || !(want_rows || mode == M_SFWD)) return KD_OK;
   }
   const bool backward = bwd && count > 0;
   const float inv_count = count > 0 ? (float)(1.0 / (double)count) : 0.f;
@@ -264,12 +288,24 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
     const uint8_t *mask_c = loss_mask ? loss_mask + c0 : nullptr;
     float *zg_c = zg ? zg + c0 * K : zg_ws;
     const float *lse_c = lse;
+    const int32_t *idx_k = idx_c;  // indices as the kernels see them (shard-local in a shard)
+    if (shard) {
+      LAUNCH(kd::KC_BUCKET,
+             kd::launch_localize_idx(idx_c, rows, K, sh.v0, V, idxloc, zg_c, stream));
+      idx_k = idxloc;
+    }
 
     if (fwd) {
       LAUNCH(kd::KC_BUCKET,
-             kd::launch_buckets(idx_c, rows, K, V, bcount, bcursor, boff, bent, stream));
+             kd::launch_buckets(idx_k, rows, K, V, bcount, bcursor, boff, bent, stream));
       LAUNCH(kd::KC_FWD_GEMM, kd::launch_fwd_gemm(dtype, W, h_c, rows, d, V, partials, L.C_alloc,
                                                   boff, bent, zg_c, K, stream));
+      if (mode == M_SFWD) {
+        LAUNCH(kd::KC_COMBINE,
+               kd::launch_shard_stats(partials, L.n_lse, L.C_alloc, zg_c, p_c, rows, K,
+                                      sh.st_m + c0, sh.st_s + c0, sh.st_pz + c0, stream));
+        continue;
+      }
       LAUNCH(kd::KC_COMBINE,
              kd::launch_combine(partials, L.n_lse, L.C_alloc, zg_c, p_c, mask_c, rows, K, inv_count,
                                 lse, sM, srow, rowterm, row_loss ? row_loss + c0 : nullptr,
@@ -286,16 +322,18 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
            kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse_c, sM, dz, L.V_pad, L.C_alloc,
                                stream));
     LAUNCH(kd::KC_SCATTER,
-           kd::launch_scatter(dtype, dz, L.C_alloc, idx_c, p_c, srow, rows, K, stream));
+           kd::launch_scatter(dtype, dz, L.C_alloc, idx_k, p_c, srow, rows, K, stream));
     LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, WT, rows, d, V, L.V_pad, L.nsplit,
                                               L.k_split, dhpart, L.d_pad, L.C_alloc, stream));
-    LAUNCH(kd::KC_DH_REDUCE, kd::launch_dh_reduce(dtype, dhpart, L.nsplit, L.C_alloc, L.d_pad,
-                                                  rows, d, (char *)dh + c0 * d * es, stream));
+    LAUNCH(kd::KC_DH_REDUCE,
+           kd::launch_dh_reduce(mode == M_SBWD ? (int)KD_F32 : dtype, dhpart, L.nsplit, L.C_alloc,
+                                L.d_pad, rows, d, (char *)dh + c0 * d * es_dh, stream));
     LAUNCH(kd::KC_DW_GEMM,
            kd::launch_dw_gemm(dtype, dz, h_c, rows, d, V, L.V_pad, L.C_alloc, dW, chunk_i > 0,
                               stream));
   }
-  if (fwd && count > 0) LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));
+  if (fwd && !shard && count > 0)
+    LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));
   return KD_OK;
 }
 
@@ -328,6 +366,84 @@ int kd_chunked_kl_bwd(const void *h, const void *W, int32_t dtype, const int32_t
                       size_t workspace_bytes, void *stream) {
   return run(M_BWD, h, W, dtype, topk_idx, topk_p, loss_mask, N, d, V, K, chunk, nullptr, dh, dW,
              nullptr, nullptr, nullptr, row_lse, grad_loss, workspace, workspace_bytes, stream);
+}
+
+int kd_vocab_shard_fwd(const void *h, const void *W_shard, int32_t dtype, const int32_t *topk_idx,
+                       const float *topk_p, int64_t N, int64_t d, int64_t V_shard,
+                       int64_t v_offset, int64_t V_total, int32_t K, int64_t chunk,
+                       float *shard_max, float *shard_sumexp, float *shard_pz, float *zg,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  ShardArgs sh;
+  sh.v0 = v_offset;
+  sh.V_total = V_total;
+  sh.st_m = shard_max;
+  sh.st_s = shard_sumexp;
+  sh.st_pz = shard_pz;
+  return run(M_SFWD, h, W_shard, dtype, topk_idx, topk_p, nullptr, N, d, V_shard, K, chunk,
+             nullptr, nullptr, nullptr, nullptr, nullptr, zg, nullptr, nullptr, workspace,
+             workspace_bytes, stream, sh);
+}
+
+int kd_vocab_shard_bwd(const void *h, const void *W_shard, int32_t dtype, const int32_t *topk_idx,
+                       const float *topk_p, const uint8_t *loss_mask, int64_t N, int64_t d,
+                       int64_t V_shard, int64_t v_offset, int64_t V_total, int32_t K,
+                       int64_t chunk, const float *row_lse, const float *grad_loss,
+                       float *dh_partial, float *dW_shard, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  ShardArgs sh;
+  sh.v0 = v_offset;
+  sh.V_total = V_total;
+  return run(M_SBWD, h, W_shard, dtype, topk_idx, topk_p, loss_mask, N, d, V_shard, K, chunk,
+             nullptr, dh_partial, dW_shard, nullptr, nullptr, nullptr, row_lse, grad_loss,
+             workspace, workspace_bytes, stream, sh);
+}
+
+int kd_vocab_shard_combine_workspace_bytes(int64_t N, size_t *bytes_out) {
+  g_err[0] = 0;
+  if (!bytes_out || N < 0) return fail(KD_E_ARG, "bad arguments");
+  *bytes_out = 256 + (size_t)rup(N * 8, 256);
+  return KD_OK;
+}
+
+int kd_vocab_shard_combine(const float *shard_max, const float *shard_sumexp,
+                           const float *shard_pz, int32_t G, const float *topk_p,
+                           const uint8_t *loss_mask, int64_t N, int32_t K, float *loss,
+                           float *row_lse, float *row_loss, void *workspace,
+                           size_t workspace_bytes, void *stream_v) {
+  g_err[0] = 0;
+  if (G < 1 || N < 0 || K < 1 || K > 65536) return fail(KD_E_ARG, "need G >= 1, N >= 0, 1 <= K <= 65536");
+  if (!loss || !workspace) return fail(KD_E_ARG, "loss and workspace are required");
+  if (N > 0 && (!shard_max || !shard_sumexp || !shard_pz || !topk_p || !row_lse))
+    return fail(KD_E_ARG, "shard statistics, topk_p and row_lse are required when N > 0");
+  if (((uintptr_t)shard_max | (uintptr_t)shard_sumexp | (uintptr_t)shard_pz | (uintptr_t)topk_p |
+       (uintptr_t)loss | (uintptr_t)row_lse | (uintptr_t)row_loss) % 4)
+    return fail(KD_E_ARG, "float arguments must be 4-byte aligned");
+  if ((uintptr_t)workspace % 256) return fail(KD_E_ARG, "workspace must be 256-byte aligned");
+  const size_t need = 256 + (size_t)rup(N * 8, 256);
+  if (workspace_bytes < need)
+    return fail(KD_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  hipStream_t stream = (hipStream_t)stream_v;
+  char *ws = (char *)workspace;
+  int *flags = (int *)ws;
+  unsigned long long *dcount = (unsigned long long *)(ws + 8);
+  double *acc = (double *)(ws + 64);
+  double *rowterm = (double *)(ws + 256);
+  LAUNCH(kd::KC_MISC, kd::launch_fill_zero(ws, 256, stream));
+  if (N == 0) {
+    LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
+    return KD_OK;
+  }
+  LAUNCH(kd::KC_VALIDATE, kd::launch_validate(nullptr, nullptr, 0, 1, loss_mask, N, flags, dcount,
+                                              stream));
+  unsigned long long hc = 0;
+  HIPCHK(hipMemcpyAsync(&hc, dcount, sizeof hc, hipMemcpyDeviceToHost, stream));
+  HIPCHK(hipStreamSynchronize(stream));
+  const int64_t count = loss_mask ? (int64_t)hc : N;
+  LAUNCH(kd::KC_COMBINE, kd::launch_shard_combine(shard_max, shard_sumexp, shard_pz, G, N, topk_p,
+                                                  loss_mask, K, row_lse, row_loss, rowterm, stream));
+  LAUNCH(kd::KC_MISC, kd::launch_accum_loss(rowterm, N, acc, stream));
+  LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));
+  return KD_OK;
 }
 
 int kd_topk_workspace_bytes(size_t *bytes_out) {

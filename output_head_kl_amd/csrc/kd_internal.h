@@ -41,7 +41,7 @@ struct Layout {
   int64_t k_split;    // vocabulary rows per split (a multiple of 256)
   int64_t nkeys;      // buckets per chunk: ceil(V / 256) * C_alloc / 256
   size_t off_flags, off_acc, off_partials, off_lse, off_sM, off_s, off_rowterm, off_zg,
-      off_dz, off_dhpart, off_bcount, off_bcursor, off_boff, off_bent, off_wt, total;
+      off_dz, off_dhpart, off_bcount, off_bcursor, off_boff, off_bent, off_wt, off_idxloc, total;
 };
 
 bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
@@ -94,6 +94,20 @@ hipError_t launch_dh_reduce(int dtype, const float *part, int nsplit, int64_t C_
 hipError_t launch_dw_gemm(int dtype, const void *dz, const void *h_c, int64_t rows, int64_t d,
                           int64_t V, int64_t V_pad, int64_t C_alloc, float *dW, int accumulate,
                           hipStream_t s);
+
+// --- vocabulary shards ---
+// loc = idx - v0 inside [v0, v0 + Vs), else -1 (skipped by buckets and scatter); zg of
+// the outside entries is set to 0.
+hipError_t launch_localize_idx(const int32_t *idx_c, int64_t rows, int32_t K, int64_t v0,
+                               int64_t Vs, int32_t *loc, float *zg_c, hipStream_t s);
+// Per token of a shard: max, sum exp(z - max) and sum_k p*z (inside the shard).
+hipError_t launch_shard_stats(const float2 *partials, int64_t n_lse, int64_t ld_part,
+                              const float *zg, const float *p_c, int64_t rows, int32_t K,
+                              float *m_out, float *s_out, float *pz_out, hipStream_t s);
+// Global logsumexp and per-token loss term from G shards' statistics ([G][N] each).
+hipError_t launch_shard_combine(const float *m, const float *sx, const float *pz, int G,
+                                int64_t N, const float *p, const uint8_t *mask, int32_t K,
+                                float *row_lse, float *row_loss, double *rowterm, hipStream_t s);
 
 // --- teacher top-K cache producer (kd_topk.hip) ---
 constexpr int kTopkMaxK = 256;

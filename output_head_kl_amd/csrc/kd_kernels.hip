@@ -963,12 +963,14 @@ __global__ void k_bucket_count(const int32_t *idx, int rows, int K, int ntm, int
   if (lds) {
     for (int i = t; i < ntm; i += blockDim.x) hist[i] = 0;
     __syncthreads();
-    for (int e = t; e < n; e += blockDim.x) atomicAdd(&hist[ip[e] >> 8], 1);
+    for (int e = t; e < n; e += blockDim.x)
+      if (ip[e] >= 0) atomicAdd(&hist[ip[e] >> 8], 1);
     __syncthreads();
     for (int i = t; i < ntm; i += blockDim.x)
       if (hist[i]) atomicAdd(&counts[i * ntn + tn], hist[i]);
   } else {
-    for (int e = t; e < n; e += blockDim.x) atomicAdd(&counts[(ip[e] >> 8) * ntn + tn], 1);
+    for (int e = t; e < n; e += blockDim.x)
+      if (ip[e] >= 0) atomicAdd(&counts[(ip[e] >> 8) * ntn + tn], 1);
   }
 }
 
@@ -1012,7 +1014,8 @@ __global__ void k_bucket_fill(const int32_t *idx, int rows, int K, int ntm, int 
   if (lds) {
     for (int i = t; i < ntm; i += blockDim.x) hist[i] = 0;
     __syncthreads();
-    for (int e = t; e < n; e += blockDim.x) atomicAdd(&hist[ip[e] >> 8], 1);
+    for (int e = t; e < n; e += blockDim.x)
+      if (ip[e] >= 0) atomicAdd(&hist[ip[e] >> 8], 1);
     __syncthreads();
     for (int i = t; i < ntm; i += blockDim.x)
       if (hist[i]) {
@@ -1022,7 +1025,9 @@ __global__ void k_bucket_fill(const int32_t *idx, int rows, int K, int ntm, int 
     __syncthreads();
   }
   for (int e = t; e < n; e += blockDim.x) {
-    const int v = ip[e], bin = v >> 8, q = e / K, r = r0 + q, k = e - q * K;
+    const int v = ip[e];
+    if (v < 0) continue;  // outside this vocabulary shard
+    const int bin = v >> 8, q = e / K, r = r0 + q, k = e - q * K;
     const int pos = lds ? base[bin] + atomicAdd(&hist[bin], 1)
                         : offsets[bin * ntn + tn] + atomicAdd(&cursor[bin * ntn + tn], 1);
     entries[pos] = (unsigned)(r & 255) | ((unsigned)(v & 255) << 8) | ((unsigned)k << 16);
@@ -1215,7 +1220,7 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, const i
     const bool has = k < K;
     const int v = has ? ir[k] : -1;
     float tot = has ? pr[k] : 0.f;
-    bool first = has;
+    bool first = has && v >= 0;  // a negative index lies outside this vocabulary shard
     for (int j0 = 0; j0 < K; j0 += 64) {
       const int jl = j0 + lane;
       const int vjl = jl < K ? ir[jl] : -1;
@@ -1283,6 +1288,121 @@ hipError_t launch_dh_reduce(int dtype, const float *part, int nsplit, int64_t C_
   else
     hipLaunchKernelGGL(k_dh_reduce<0>, dim3(blocks), dim3(256), 0, s, part, nsplit,
                        (long long)(C_alloc * d_pad), (long long)d_pad, (int)rows, (int)d, dh);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Vocabulary shards (one GPU's share of a tensor-parallel output head)
+// ---------------------------------------------------------------------------------
+// loc[r][k] = idx - v0 when v0 <= idx < v0 + Vs, else -1; zg of outside entries = 0.
+__global__ void k_localize_idx(const int32_t *idx, long long n, int v0, int Vs, int32_t *loc,
+                               float *zg) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int v = idx[i] - v0;
+    const bool in = v >= 0 && v < Vs;
+    loc[i] = in ? v : -1;
+    if (!in) zg[i] = 0.f;
+  }
+}
+
+hipError_t launch_localize_idx(const int32_t *idx_c, int64_t rows, int32_t K, int64_t v0,
+                               int64_t Vs, int32_t *loc, float *zg_c, hipStream_t s) {
+  const long long n = rows * (long long)K;
+  const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL(k_localize_idx, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, s, idx_c, n,
+                     (int)v0, (int)Vs, loc, zg_c);
+  return hipGetLastError();
+}
+
+// Per token of a shard: max and sum exp(z - max) over the shard's logits (folded from
+// the forward GEMM's per-slice partials, as in k_combine) and sum_k p * z over the
+// teacher entries inside the shard (zg is 0 for the others).
+__global__ __launch_bounds__(64 * kCombWaves) void k_shard_stats(
+    const float2 *part, int n_lse, long long ld, const float *zg, const float *p, int rows,
+    int K, float *m_out, float *s_out, float *pz_out) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = blockIdx.x * 64 + lane;
+  const bool live = r < rows;
+  float m = -INFINITY, sum = 0.f;
+  if (live) {
+    for (int t = w; t < n_lse; t += kCombWaves) {
+      const float2 q = part[(long long)t * ld + r];
+      if (q.y == 0.f) continue;
+      if (q.x > m) {
+        sum = sum * fast_exp2((m - q.x) * kLog2e) + q.y;
+        m = q.x;
+      } else {
+        sum += q.y * fast_exp2((q.x - m) * kLog2e);
+      }
+    }
+  }
+  __shared__ float sm[kCombWaves][64], ss[kCombWaves][64];
+  __shared__ double sd[kCombWaves][64];
+  sm[w][lane] = m;
+  ss[w][lane] = sum;
+  double PZ = 0.0;
+  if (live)
+    for (int k = w; k < K; k += kCombWaves)
+      PZ += (double)p[(long long)r * K + k] * (double)zg[(long long)r * K + k];
+  sd[w][lane] = PZ;
+  __syncthreads();
+  if (w == 0 && live) {
+    float M = sm[0][lane];
+    for (int i = 1; i < kCombWaves; ++i) M = fmaxf(M, sm[i][lane]);
+    float S = 0.f;
+    for (int i = 0; i < kCombWaves; ++i)
+      if (ss[i][lane] != 0.f) S += ss[i][lane] * fast_exp2((sm[i][lane] - M) * kLog2e);
+    double pz = 0.0;
+    for (int i = 0; i < kCombWaves; ++i) pz += sd[i][lane];
+    m_out[r] = M;
+    s_out[r] = S;
+    pz_out[r] = (float)pz;
+  }
+}
+
+hipError_t launch_shard_stats(const float2 *partials, int64_t n_lse, int64_t ld_part,
+                              const float *zg, const float *p_c, int64_t rows, int32_t K,
+                              float *m_out, float *s_out, float *pz_out, hipStream_t s) {
+  hipLaunchKernelGGL(k_shard_stats, dim3(cdiv(rows, 64)), dim3(64 * kCombWaves), 0, s, partials,
+                     (int)n_lse, (long long)ld_part, zg, p_c, (int)rows, (int)K, m_out, s_out,
+                     pz_out);
+  return hipGetLastError();
+}
+
+// Combine of G shards' statistics per token: lse = M + log sum_g s_g exp(m_g - M),
+// l = sum_k p log p - sum_g pz_g + (sum_k p) lse; rowterm = mask ? l : 0.
+__global__ void k_shard_combine(const float *m, const float *sx, const float *pz, int G,
+                                long long N, const float *p, const uint8_t *mask, int K,
+                                float *row_lse, float *row_loss, double *rowterm) {
+  const long long r = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (r >= N) return;
+  float M = -INFINITY;
+  for (int g = 0; g < G; ++g) M = fmaxf(M, m[g * N + r]);
+  double S = 0.0, PZ = 0.0;
+  for (int g = 0; g < G; ++g) {
+    if (sx[g * N + r] != 0.f) S += (double)sx[g * N + r] * (double)fast_exp2((m[g * N + r] - M) * kLog2e);
+    PZ += (double)pz[g * N + r];
+  }
+  const float lse = M + logf((float)S);
+  double H = 0.0, Ms = 0.0;
+  for (int k = 0; k < K; ++k) {
+    const double q = p[r * K + k];
+    Ms += q;
+    if (q > 0.0) H += q * log(q);
+  }
+  const double ell = H - PZ + Ms * (double)lse;
+  const bool on = mask ? mask[r] != 0 : true;
+  if (row_lse) row_lse[r] = lse;
+  if (row_loss) row_loss[r] = on ? (float)ell : 0.f;
+  rowterm[r] = on ? ell : 0.0;
+}
+
+hipError_t launch_shard_combine(const float *m, const float *sx, const float *pz, int G,
+                                int64_t N, const float *p, const uint8_t *mask, int32_t K,
+                                float *row_lse, float *row_loss, double *rowterm, hipStream_t s) {
+  hipLaunchKernelGGL(k_shard_combine, dim3(cdiv(N, 256)), dim3(256), 0, s, m, sx, pz, G,
+                     (long long)N, p, mask, (int)K, row_lse, row_loss, rowterm);
   return hipGetLastError();
 }
 

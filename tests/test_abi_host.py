@@ -199,3 +199,26 @@ def test_topk_rejects_bad_calls_on_host(lib, kw, code):
 
 def test_topk_with_no_rows_does_nothing(lib):
     assert _call_topk(lib, N=0, logits=None, idx=None, p=None) == OK
+
+
+def _call_shard_fwd(lib, **kw):
+    base = dict(h=0x100000, W=0x200000, dtype=1, idx=0x300000, p=0x400000, N=64, d=64, Vs=500,
+                v0=500, Vt=1000, K=4, chunk=32, m=0x500000, s=0x600000, pz=0x700000, zg=None,
+                ws=0x800000, wsb=1 << 40, stream=None)
+    base.update(kw)
+    b = base
+    return lib.kd_vocab_shard_fwd(b["h"], b["W"], b["dtype"], b["idx"], b["p"], b["N"], b["d"],
+                                  b["Vs"], b["v0"], b["Vt"], b["K"], b["chunk"], b["m"], b["s"],
+                                  b["pz"], b["zg"], b["ws"], b["wsb"], b["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v0=600), E_ARG),            # shard runs past the vocabulary
+    (dict(v0=-1), E_ARG),
+    (dict(Vt=400), E_ARG),            # vocabulary smaller than the shard
+    (dict(m=None), E_ARG),            # statistics outputs are required
+    (dict(Vt=1 << 25, v0=0), E_ARG),  # vocabulary above 2^24
+])
+def test_shard_forward_rejects_bad_shards_on_host(lib, kw, code):
+    assert _call_shard_fwd(lib, **kw) == code
+    assert lib.kd_last_error()

@@ -1,0 +1,118 @@
+"""Vocabulary shards through the C ABI: G shards of W run forward, the statistics are
+combined, each shard runs backward, and the reassembled loss, logsumexp, dh (sum of
+the float32 partials) and dW (the shards' rows) match the oracle of the whole head."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, grad_err, max_abs_rel, rel, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_shards(inp, bounds, torch, chunk, g=None):
+    import output_head_kl_amd as kd
+    h, W, idx, p, mask = to_device(inp, torch)
+    V = inp.cfg.V
+    stats = [kd.vocab_shard_fwd(h, W[a:b].contiguous(), idx, p, a, V, chunk=chunk)
+             for a, b in bounds]
+    m, s, pz = (torch.stack([st[i] for st in stats]) for i in range(3))
+    loss, row_lse, row_loss = kd.vocab_shard_combine(m, s, pz, p, mask)
+    gt = None if g is None else torch.tensor([g], dtype=torch.float32, device="cuda")
+    dh = torch.zeros((inp.cfg.N, inp.cfg.d), dtype=torch.float32, device="cuda")
+    dWs = []
+    for a, b in bounds:
+        dhp, dWp = kd.vocab_shard_bwd(h, W[a:b].contiguous(), idx, p, row_lse, a, V, gt, mask,
+                                      chunk=chunk)
+        dh += dhp            # the all-reduce of the partials (test side)
+        dWs.append(dWp)
+    torch.cuda.synchronize()
+    return dict(loss=to_f64(loss, torch), row_lse=to_f64(row_lse, torch),
+                row_loss=to_f64(row_loss, torch), dh=to_f64(dh, torch),
+                dW=to_f64(torch.cat(dWs), torch))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_four_uneven_shards_match_the_whole_head(torch_cuda, dtype):
+    inp = synth.make(1, seed=61, N=700, d=264, V=3001, K=7, chunk=300, dtype=dtype)
+    inp.mask[[0, 5, 299, 300, 699]] = 0
+    inp.idx[3, 1] = inp.idx[3, 0]          # a repeated index (scatter-add within a shard)
+    bounds = [(0, 700), (700, 1500), (1500, 2600), (2600, 3001)]
+    got = _run_shards(inp, bounds, torch_cuda, chunk=300)
+    ref = oracle.forward_backward(inp.h64(), inp.W64(), inp.idx, inp.p, inp.mask)
+    tol = TOL[dtype]
+    errs = dict(loss=rel(got["loss"][0], ref["loss"]),
+                lse=max_abs_rel(got["row_lse"], ref["row_lse"]),
+                row_loss=max_abs_rel(got["row_loss"], ref["row_loss"]),
+                dh=grad_err(dtype, got["dh"], ref["dh"]),
+                dW=grad_err(dtype, got["dW"], ref["dW"]))
+    print(dtype, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert errs["loss"] <= tol["loss"] and errs["lse"] <= tol["loss"], errs
+    assert errs["row_loss"] <= 10 * tol["loss"], errs
+    assert errs["dh"] <= tol["grad"] and errs["dW"] <= tol["grad"], errs
+    assert np.all(got["dh"][inp.mask == 0] == 0.0)
+
+
+def test_one_shard_is_the_fused_call(torch_cuda):
+    import output_head_kl_amd as kd
+    torch = torch_cuda
+    inp = synth.make(0, seed=12, N=400, chunk=128)
+    got = _run_shards(inp, [(0, inp.cfg.V)], torch, chunk=128)
+    h, W, idx, p, mask = to_device(inp, torch)
+    loss, dh, dW = kd.fwd_bwd(h, W, idx, p, mask, chunk=128)
+    torch.cuda.synchronize()
+    assert rel(got["loss"][0], float(loss[0])) < 1e-6
+    assert max_abs_rel(got["dh"], to_f64(dh, torch)) < 1e-6
+    assert max_abs_rel(got["dW"], to_f64(dW, torch)) < 1e-6
+
+
+def test_upstream_gradient_scales_the_shard_gradients(torch_cuda):
+    inp = synth.make(0, seed=14, N=300, chunk=128)
+    bounds = [(0, 3000), (3000, 8192)]
+    a = _run_shards(inp, bounds, torch_cuda, chunk=128)
+    b = _run_shards(inp, bounds, torch_cuda, chunk=128, g=-1.5)
+    assert max_abs_rel(b["dh"], -1.5 * a["dh"]) < 1e-6
+    assert max_abs_rel(b["dW"], -1.5 * a["dW"]) < 1e-6
+
+
+def test_full_size_shard_of_eight(torch_cuda):
+    """One GPU's share at V/8 of the 128256 vocabulary, N = 4096 tokens: the shard's
+    statistics on 256 sampled rows against the oracle restricted to that shard."""
+    import output_head_kl_amd as kd
+    torch = torch_cuda
+    inp = synth.make(1)
+    V, Vs = inp.cfg.V, inp.cfg.V // 8
+    a, b = 3 * Vs, 4 * Vs
+    h, W, idx, p, mask = to_device(inp, torch)
+    m, s, pz = kd.vocab_shard_fwd(h, W[a:b].contiguous(), idx, p, a, V, chunk=inp.cfg.chunk)
+    torch.cuda.synchronize()
+    rows = synth.subset_rows(inp.cfg, inp.seed, 256)
+    H = inp.h64()[rows]
+    Z = H @ inp.W64()[a:b].T
+    rm = Z.max(axis=1)
+    rs = np.exp(Z - rm[:, None]).sum(axis=1)
+    ii, pp = inp.idx[rows], inp.p[rows].astype(np.float64)
+    inside = (ii >= a) & (ii < b)
+    zloc = np.where(inside, np.take_along_axis(Z, np.clip(ii - a, 0, Vs - 1), 1), 0.0)
+    rpz = (pp * zloc).sum(axis=1)
+    gm, gs, gp = (to_f64(t, torch)[rows] for t in (m, s, pz))
+    # the row max is a plain float32 max of bf16-input GEMM values; sums compared relatively
+    assert max_abs_rel(gm, rm) < 2e-3
+    assert rel_vec(gs * np.exp(gm - rm), rs) < 2e-3
+    assert np.abs(gp - rpz).max() <= 2e-3 * np.abs(rpz).max() + 1e-6
+
+
+def rel_vec(a, b):
+    return float(np.abs(a - b).max() / np.abs(b).max())
+
+
+def test_index_outside_the_vocabulary_is_rejected(torch_cuda):
+    import output_head_kl_amd as kd
+    torch = torch_cuda
+    inp = synth.make(0, seed=2, N=64, chunk=64)
+    inp.idx[5, 3] = inp.cfg.V + 7
+    h, W, idx, p, mask = to_device(inp, torch)
+    with pytest.raises(kd.KDError) as e:
+        kd.vocab_shard_fwd(h, W[:1000].contiguous(), idx, p, 0, inp.cfg.V, chunk=64)
+    assert e.value.code == 2
