@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--shard", type=int, default=0,
                     help="time one GPU's share of a vocabulary-sharded head: rows [0, V/G) of W "
                          "with the full token batch (forward statistics + backward); G = value")
+    ap.add_argument("--torch-baselines", action="store_true",
+                    help="context only: peak memory and time of a dense and a forward-chunked "
+                         "PyTorch implementation of the same loss (torch autograd, hipBLASLt "
+                         "GEMMs) next to the fused library call, N = 4K..128K; prints one JSON line")
     ap.add_argument("--topk", action="store_true",
                     help="time the teacher top-K cache producer (kd_teacher_topk) on N=32768 rows "
                          "of V=128256 bf16 teacher logits, K=100; prints one JSON line")
@@ -186,6 +190,65 @@ def bench_topk(args):
                                "sample": f"the first {rows} rows of the same logits, float64 numpy "
                                          f"(full-row stable sort), {dt:.1f} s"}
     print(json.dumps(res), flush=True)
+
+
+def torch_baselines():
+    """The loss written with torch ops, as a dense and as a forward-chunked autograd graph,
+    for the pages' memory comparison (output head only).  Not part of the library: these
+    run torch's kernels; the library's own call is timed beside them."""
+    import torch
+
+    import output_head_kl_amd as kd
+    d, V, K, chunk = 3072, 128256, 100, 2048
+    g = torch.Generator(device="cuda").manual_seed(20260804)
+    W0 = torch.randn(V, d, device="cuda", generator=g, dtype=torch.bfloat16) * (2.0 / d ** 0.5)
+
+    def loss_of(hc, W, idx, p, mask, count):
+        z = torch.mm(hc, W.t()).float()
+        lq = torch.log_softmax(z, dim=-1).gather(1, idx.long())
+        ell = (torch.xlogy(p, p) - p * lq).sum(1)
+        return (ell * mask).sum() / count
+
+    results = []
+    for N in [4096, 16384, 32768, 65536, 131072]:
+        h0 = torch.randn(N, d, device="cuda", generator=g, dtype=torch.bfloat16)
+        idx = torch.randint(0, V, (N, K), device="cuda", generator=g, dtype=torch.int32)
+        p = torch.rand(N, K, device="cuda", generator=g) / K
+        mask = torch.ones(N, device="cuda")
+        row = {"N": N}
+        for kind in ["dense", "forward_chunked", "fused_library"]:
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            try:
+                t0 = time.perf_counter()
+                if kind == "fused_library":
+                    out = kd.fwd_bwd(h0, W0, idx, p, mask.to(torch.uint8), chunk=chunk)
+                    del out
+                else:
+                    h = h0.detach().requires_grad_(True)
+                    W = W0.detach().requires_grad_(True)
+                    if kind == "dense":
+                        loss = loss_of(h, W, idx, p, mask, float(N))
+                    else:  # chunks in the forward; autograd keeps every chunk's logits
+                        loss = sum(loss_of(h[c:c + chunk], W, idx[c:c + chunk], p[c:c + chunk],
+                                           mask[c:c + chunk], float(N))
+                                   for c in range(0, N, chunk))
+                    loss.backward()
+                    del loss, h, W
+                torch.cuda.synchronize()
+                row[kind] = {"peak_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
+                             "s": round(time.perf_counter() - t0, 3)}
+            except torch.cuda.OutOfMemoryError:
+                row[kind] = "out of memory"
+            torch.cuda.empty_cache()
+            print(f"[baselines] N={N} {kind}: {row[kind]}", file=sys.stderr, flush=True)
+        results.append(row)
+        del h0, idx, p, mask
+    print(json.dumps({"torch_baselines": {"d": d, "V": V, "K": K, "chunk": chunk, "dtype": "bf16",
+                                          "note": "one call each (first call includes "
+                                                  "library and kernel warm-up)",
+                                          "rows": results}}), flush=True)
 
 
 def memory_sweep():
@@ -361,6 +424,9 @@ def main():
     args = parse()
     if args.memory_sweep:
         memory_sweep()
+        return
+    if args.torch_baselines:
+        torch_baselines()
         return
     if args.topk:
         if args.gpus != 1:
