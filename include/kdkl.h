@@ -89,6 +89,10 @@ int kd_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk
  *   d <= 2^20, V <= 2^24, N*d and N*K below 2^62.  N == 0 writes loss = 0 and dW = 0.
  * chunk is the number of token rows whose logits are live at once; the last
  *   chunk may be partial; results do not depend on it beyond float rounding.
+ *   Each chunk's backward runs right after its forward, while the chunk's logits
+ *   (kept as exp(z - max) in the workspace) are still live, so this call needs no
+ *   second logits GEMM; kd_chunked_kl_bwd, which runs after the whole forward,
+ *   recomputes them.
  * stream: a hipStream_t (NULL = the null stream).  All work is enqueued on it.
  *   The call synchronises the stream once, after validating the teacher entries
  *   and counting the mask; the rest is asynchronous and the outputs are ready when
@@ -137,7 +141,8 @@ int kd_chunked_kl_fwd(const void *h, const void *W, int32_t dtype,
  *                                    same h, W and chunk (required when N > 0)
  *   grad_loss [1]  float32  device   g, read on the device (no host synchronisation)
  * With g = 1 and row_lse from kd_chunked_kl_fwd, dh and dW equal those of
- * kd_chunked_kl_fwd_bwd bit for bit.  Teacher entries are validated again (one stream
+ * kd_chunked_kl_fwd_bwd up to rounding (that call derives dz from its forward's
+ * exponentials rather than recomputed logits).  Teacher entries are validated again (one stream
  * synchronisation); count == 0 or N == 0 gives dh = 0 and dW = 0.  Same workspace
  * (kd_workspace_bytes), stream behaviour and errors as kd_chunked_kl_fwd_bwd.
  */

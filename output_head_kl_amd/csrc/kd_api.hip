@@ -4,8 +4,10 @@
 // the device.  The call then validates the teacher entries and counts the loss mask
 // on the device, synchronises the stream once to read the result, and enqueues the
 // per-chunk sequence: forward GEMM (per-tile max / sum-exp), gather at the teacher's
-// indices, logsumexp + loss, backward GEMM (recomputed logits -> dz), sparse
-// correction of dz, dh GEMM + reduction, dW GEMM.  Only one chunk's dz is live.
+// indices, logsumexp + loss, dz, sparse correction of dz, dh GEMM + reduction, dW GEMM.
+// The fused call takes dz from the exp(z - max) its forward GEMM kept in the dz buffer
+// (one streaming rescale once the logsumexp is known); the backward-only call recomputes
+// the logits with a second GEMM.  Only one chunk's dz (in two layouts) is live.
 #include "kd_internal.h"
 #include "kdkl.h"
 
@@ -41,7 +43,7 @@ std::mutex g_prof_mu;
 
 const char *const kClassNames[kd::KC_COUNT] = {
     "validate", "fwd_gemm_lse", "bucket", "combine_lse_loss", "bwd_gemm_dz",
-    "scatter",  "dh_gemm",      "dh_reduce", "dw_gemm",      "w_transpose", "teacher_topk", "misc"};
+    "scatter",  "dh_gemm",      "dh_reduce", "dw_gemm",      "transpose", "teacher_topk", "dz_rescale", "misc"};
 
 #define HIPCHK(expr)                                                                 \
   do {                                                                               \
@@ -136,6 +138,8 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->off_bent = take((size_t)L->C_alloc * K * 4);
   L->off_wt = take(dtype == KD_BF16 ? (size_t)L->V_pad * d * 2 : 0);
   L->off_idxloc = take((size_t)L->C_alloc * K * 4);
+  L->off_dzt = take(dtype == KD_BF16 ? (size_t)L->V_pad * L->C_alloc * 2 : 0);
+  L->off_ht = take(dtype == KD_BF16 ? (size_t)d * L->C_alloc * 2 : 0);
   L->total = off;
   return true;
 }
@@ -232,6 +236,8 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
   double *rowterm = (double *)(ws + L.off_rowterm);
   float *zg_ws = (float *)(ws + L.off_zg);
   void *dz = ws + L.off_dz;
+  void *dzt = dtype == KD_BF16 ? (void *)(ws + L.off_dzt) : nullptr;
+  void *ht = dtype == KD_BF16 ? (void *)(ws + L.off_ht) : nullptr;
   float *dhpart = (float *)(ws + L.off_dhpart);
   int *bcount = (int *)(ws + L.off_bcount);
   int *bcursor = (int *)(ws + L.off_bcursor);
@@ -298,8 +304,11 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
     if (fwd) {
       LAUNCH(kd::KC_BUCKET,
              kd::launch_buckets(idx_k, rows, K, V, bcount, bcursor, boff, bent, stream));
+      // the fused call keeps this chunk's exp(z - max) for its backward (no recompute)
+      void *u = (mode == M_FUSED && count > 0) ? dz : nullptr;
       LAUNCH(kd::KC_FWD_GEMM, kd::launch_fwd_gemm(dtype, W, h_c, rows, d, V, partials, L.C_alloc,
-                                                  boff, bent, zg_c, K, stream));
+                                                  boff, bent, zg_c, K, u, L.V_pad, L.C_alloc,
+                                                  stream));
       if (mode == M_SFWD) {
         LAUNCH(kd::KC_COMBINE,
                kd::launch_shard_stats(partials, L.n_lse, L.C_alloc, zg_c, p_c, rows, K,
@@ -318,19 +327,23 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
                                                   srow, stream));
     }
     if (!backward) continue;
-    LAUNCH(kd::KC_BWD_GEMM,
-           kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse_c, sM, dz, L.V_pad, L.C_alloc,
-                               stream));
+    if (mode == M_FUSED)
+      LAUNCH(kd::KC_RESCALE, kd::launch_rescale_dz(dtype, dz, dzt, partials, lse_c, sM, rows, V,
+                                                   L.V_pad, L.C_alloc, stream));
+    else
+      LAUNCH(kd::KC_BWD_GEMM, kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse_c, sM, dz, dzt,
+                                                  L.V_pad, L.C_alloc, stream));
     LAUNCH(kd::KC_SCATTER,
-           kd::launch_scatter(dtype, dz, L.C_alloc, idx_k, p_c, srow, rows, K, stream));
+           kd::launch_scatter(dtype, dz, dzt, L.C_alloc, idx_k, p_c, srow, rows, K, stream));
     LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, WT, rows, d, V, L.V_pad, L.nsplit,
                                               L.k_split, dhpart, L.d_pad, L.C_alloc, stream));
     LAUNCH(kd::KC_DH_REDUCE,
            kd::launch_dh_reduce(mode == M_SBWD ? (int)KD_F32 : dtype, dhpart, L.nsplit, L.C_alloc,
                                 L.d_pad, rows, d, (char *)dh + c0 * d * es_dh, stream));
-    LAUNCH(kd::KC_DW_GEMM,
-           kd::launch_dw_gemm(dtype, dz, h_c, rows, d, V, L.V_pad, L.C_alloc, dW, chunk_i > 0,
-                              stream));
+    if (ht)
+      LAUNCH(kd::KC_TRANSPOSE, kd::launch_transpose_h(h_c, rows, d, L.C_alloc, ht, stream));
+    LAUNCH(kd::KC_DW_GEMM, kd::launch_dw_gemm(dtype, dz, dzt, h_c, ht, rows, d, V, L.V_pad,
+                                              L.C_alloc, dW, chunk_i > 0, stream));
   }
   if (fwd && !shard && count > 0)
     LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));

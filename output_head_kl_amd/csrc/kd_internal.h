@@ -24,8 +24,9 @@ enum KClass {
   KC_DH_GEMM,      // dh partials (split over the vocabulary)
   KC_DH_REDUCE,    // dh partials summed and rounded
   KC_DW_GEMM,      // dW accumulation
-  KC_TRANSPOSE,    // W copied to vocabulary-contiguous blocks for the dh GEMM
+  KC_TRANSPOSE,    // W and h transposed for the dh and dW GEMMs
   KC_TOPK,         // teacher top-K cache producer
+  KC_RESCALE,      // single-sweep backward: exp(z - max) rescaled into dz
   KC_MISC,         // fills, loss accumulation and finalisation
   KC_COUNT
 };
@@ -41,7 +42,8 @@ struct Layout {
   int64_t k_split;    // vocabulary rows per split (a multiple of 256)
   int64_t nkeys;      // buckets per chunk: ceil(V / 256) * C_alloc / 256
   size_t off_flags, off_acc, off_partials, off_lse, off_sM, off_s, off_rowterm, off_zg,
-      off_dz, off_dhpart, off_bcount, off_bcursor, off_boff, off_bent, off_wt, off_idxloc, total;
+      off_dz, off_dhpart, off_bcount, off_bcursor, off_boff, off_bent, off_wt, off_idxloc,
+      off_dzt, off_ht, total;
 };
 
 bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
@@ -57,11 +59,17 @@ hipError_t launch_validate(const int32_t *idx, const float *p, int64_t NK, int64
 // counts must be zero on entry and are left zero.
 hipError_t launch_buckets(const int32_t *idx_c, int64_t rows, int32_t K, int64_t V, int *counts,
                           int *cursor, int *offsets, unsigned *entries, hipStream_t s);
-// Logits GEMM with the per-tile (max, sum exp) epilogue and the fused gather into zg.
+// Logits GEMM with the per-tile (max, sum exp) epilogue and the fused gather into zg;
+// with u non-null it also writes u = exp(z - max of the token's 128-row group) into the
+// dz buffer (rows v < V_pad, tokens c < rows) for launch_rescale_dz.
 hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows,
                            int64_t d, int64_t V, float2 *partials, int64_t ld_part,
                            const int *boff, const unsigned *bent, float *zg, int32_t K,
-                           hipStream_t s);
+                           void *u, int64_t V_pad, int64_t C_alloc, hipStream_t s);
+// dz = sM * exp(m_g - lse) * u in place (and dzT for bf16), from the forward's partials.
+hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, const float2 *partials,
+                             const float *lse, const float *sM, int64_t rows, int64_t V,
+                             int64_t V_pad, int64_t C_alloc, hipStream_t s);
 hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part,
                           const float *zg, const float *p_c, const uint8_t *mask_c,
                           int64_t rows, int32_t K, float inv_count, float *lse, float *sM,
@@ -75,12 +83,17 @@ hipError_t launch_accum_loss(const double *rowterm, int64_t rows, double *acc, h
 hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s);
 // dz is stored as blocks of 256 vocabulary columns: element (c, v) at
 // dz[(v / 256) * C_alloc * 256 + c * 256 + v % 256].
+// bf16 also writes dzT, the same values token-contiguous: element (c, v) at
+// dzT[v * C_alloc + c] for v < V_pad, c < rows.
 hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
-                           int64_t V, const float *lse, const float *sM, void *dz,
+                           int64_t V, const float *lse, const float *sM, void *dz, void *dzt,
                            int64_t V_pad, int64_t C_alloc, hipStream_t s);
-hipError_t launch_scatter(int dtype, void *dz, int64_t C_alloc, const int32_t *idx_c,
+hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t C_alloc, const int32_t *idx_c,
                           const float *p_c, const float *srow, int64_t rows, int32_t K,
                           hipStream_t s);
+// h chunk [rows][d] bf16 -> hT [d][C_alloc] (columns c < rows written).
+hipError_t launch_transpose_h(const void *h_c, int64_t rows, int64_t d, int64_t C_alloc, void *ht,
+                              hipStream_t s);
 // W^T in blocks of 256 vocabulary entries (bf16 only): element (v, j) of W at
 // WT[(v / 256) * d * 256 + j * 256 + v % 256], zero for V <= v < V_pad.
 hipError_t launch_transpose_w(const void *W, int64_t V, int64_t d, int64_t V_pad, void *WT,
@@ -91,9 +104,10 @@ hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, const void *
                           float *part, int64_t d_pad, int64_t C_alloc, hipStream_t s);
 hipError_t launch_dh_reduce(int dtype, const float *part, int nsplit, int64_t C_alloc,
                             int64_t d_pad, int64_t rows, int64_t d, void *dh, hipStream_t s);
-hipError_t launch_dw_gemm(int dtype, const void *dz, const void *h_c, int64_t rows, int64_t d,
-                          int64_t V, int64_t V_pad, int64_t C_alloc, float *dW, int accumulate,
-                          hipStream_t s);
+// dW += dz^T h: bf16 reads dzT and hT (both token-contiguous), fp32 reads dz and h.
+hipError_t launch_dw_gemm(int dtype, const void *dz, const void *dzt, const void *h_c,
+                          const void *ht, int64_t rows, int64_t d, int64_t V, int64_t V_pad,
+                          int64_t C_alloc, float *dW, int accumulate, hipStream_t s);
 
 // --- vocabulary shards ---
 // loc = idx - v0 inside [v0, v0 + Vs), else -1 (skipped by buckets and scatter); zg of

@@ -315,7 +315,10 @@ void gemm_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
 //  * per (token, 128 vocabulary rows): max and sum of exp(z - max) -> part;
 //  * gather: the tile's teacher hits (bucket key = vocabulary tile * token tiles + token
 //    tile, entries packed c_local | v_local << 8 | k << 16) read z from the tile, staged
-//    through LDS in four slices of 64 vocabulary rows ([256 tokens][68] fp32, 68 KB).
+//    through LDS in four slices of 64 vocabulary rows ([256 tokens][68] fp32, 68 KB);
+//  * optionally (u != null) u = exp(z - max) itself, in dz's layout, for the single-sweep
+//    backward (k_rescale_dz turns it into dz once the logsumexp is known).
+template <int DT>
 struct EpiFwdLse {
   float2 *part;   // [n_lse][ld] (max, sum exp(z - max)) per 128 vocabulary rows
   long long ld;
@@ -325,9 +328,13 @@ struct EpiFwdLse {
   int ntn;                // token tiles in the chunk
   float *zg;              // [rows][K] logits at the teacher's indices
   int K;
-  template <int NCB>
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][NCB], int m0, int n0, int lane,
+  void *u;                // null, or dz's buffer: [V_pad/256][C_alloc][256]
+  long long ts;           // C_alloc * 256
+  int V_pad;
+  template <int NRB, int NCB>
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
                                              int, char *smem) const {
+    static_assert(NRB == 4, "one (max, sum) partial per 128 vocabulary rows");
     if (m0 < V) {
       const bool full = m0 + 128 <= V;
       const int vl = m0 + (lane >> 5) * 4;
@@ -343,17 +350,54 @@ struct EpiFwdLse {
           }
         mx = halves_max(mx);
         const float mx2 = mx * kLog2e;
+        const int c = n0 + cb * 32 + (lane & 31);
+        const bool keep = u != nullptr && c < rows;
         float s = 0.f;
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
-            if (full || v < V) s += fast_exp2(fmaf(acc[rb][cb][i], kLog2e, -mx2));
+          for (int g = 0; g < 4; ++g) {
+            const int v0 = vl + rb * 32 + g * 8;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[e] = (full || v0 + e < V) ? fast_exp2(fmaf(acc[rb][cb][g * 4 + e], kLog2e, -mx2))
+                                          : 0.f;
+              s += x[e];
+            }
+            if (keep && v0 < V_pad) {
+              if (DT == 1) {
+                const u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                *(u32x2 *)((unsigned short *)u + (long long)(v0 >> 8) * ts + c * 256 +
+                           (v0 & 255)) = pk;
+              } else {
+                *(f32x4 *)((float *)u + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) =
+                    f32x4{x[0], x[1], x[2], x[3]};
+              }
+            }
           }
         s = halves_sum(s);
-        const int c = n0 + cb * 32 + (lane & 31);
         if (lane < 32 && c < rows) part[(long long)(m0 / kLseRows) * ld + c] = make_float2(mx, s);
+      }
+    } else if (u != nullptr) {
+      // rows V <= v < V_pad of a tile wholly past V: u = 0
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int c = n0 + cb * 32 + (lane & 31);
+        if (c >= rows) continue;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int v0 = m0 + (lane >> 5) * 4 + rb * 32 + g * 8;
+            if (v0 >= V_pad) continue;
+            if (DT == 1)
+              *(u32x2 *)((unsigned short *)u + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) =
+                  u32x2{0u, 0u};
+            else
+              *(f32x4 *)((float *)u + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) =
+                  f32x4{0.f, 0.f, 0.f, 0.f};
+          }
       }
     }
     // fused gather (the same branch for every wave of the workgroup)
@@ -395,34 +439,55 @@ struct EpiFwdLse {
 };
 
 // Backward: dz[c][v] = sM[c] * exp(z - lse[c]) for v < V, 0 for V <= v < V_pad.
+// bf16 also writes dzT[v][c] (token-contiguous, for the dW GEMM): lanes c and c ^ 1
+// swap halves of their packed values so that each writes two tokens of two rows.
 template <int DT>
 struct EpiBwdDz {
   void *dz;      // blocks of 256 vocabulary columns: [V_pad/256][C_alloc][256]
   long long ts;  // C_alloc * 256
   const float *lse, *sM;
-  int V, rows;
-  template <int NCB>
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][NCB], int m0, int n0, int lane,
+  int V, rows, V_pad;
+  unsigned short *dzt;  // [V_pad][ldt] (bf16 only)
+  long long ldt;
+  template <int NRB, int NCB>
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
                                              int, char *) const {
     const int vl = m0 + (lane >> 5) * 4;
+    const bool odd = lane & 1;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
+      // tokens rows <= c < C_alloc get zeros: the dW GEMM reads dzT in 8-token chunks
       const int c = n0 + cb * 32 + (lane & 31);
-      if (c >= rows) continue;
-      const float l2 = lse[c] * kLog2e;
-      const float a = sM[c];
+      const bool cv = c < rows;
+      float l2 = 0.f, a = 0.f;
+      if (cv) {
+        l2 = lse[c] * kLog2e;
+        a = sM[c];
+      }
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int v0 = vl + rb * 32 + g * 8;
+          if (v0 >= V_pad) continue;  // V_pad is a multiple of 4
           float x[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            x[e] = (v0 + e < V) ? a * fast_exp2(fmaf(acc[rb][cb][g * 4 + e], kLog2e, -l2)) : 0.f;
+            x[e] = (cv && v0 + e < V) ? a * fast_exp2(fmaf(acc[rb][cb][g * 4 + e], kLog2e, -l2))
+                                      : 0.f;
           if (DT == 1) {
             u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
             *(u32x2 *)((unsigned short *)dz + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) = pk;
+            // even lane: rows v0, v0+1 at tokens (c, c+1); odd lane: rows v0+2, v0+3 at
+            // tokens (c-1, c)
+            const unsigned got = __shfl_xor(odd ? pk[0] : pk[1], 1, 64);
+            const unsigned mine = odd ? pk[1] : pk[0];
+            const unsigned lo = odd ? got : mine, hi = odd ? mine : got;
+            const unsigned r0 = (lo & 0xFFFFu) | (hi << 16);
+            const unsigned r1 = (lo >> 16) | (hi & 0xFFFF0000u);
+            unsigned short *q = dzt + (long long)(v0 + (odd ? 2 : 0)) * ldt + (c & ~1);
+            *(unsigned *)q = r0;
+            *(unsigned *)(q + ldt) = r1;
           } else {
             *(f32x4 *)((float *)dz + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) =
                 f32x4{x[0], x[1], x[2], x[3]};
@@ -437,8 +502,8 @@ struct EpiDhPart {
   float *part;
   long long split_stride, ld;  // C_alloc*d_pad, d_pad
   int rows;
-  template <int NCB>
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][NCB], int m0, int n0, int lane,
+  template <int NRB, int NCB>
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
                                              int split, char *) const {
     float *base = part + split * split_stride;
     const int jl = m0 + (lane >> 5) * 4;
@@ -447,10 +512,11 @@ struct EpiDhPart {
       const int c = n0 + cb * 32 + (lane & 31);
       if (c >= rows) continue;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int j = jl + rb * 32 + g * 8;
+          if (j >= ld) continue;  // d_pad is a multiple of 4
           const f32x4 v = {acc[rb][cb][g * 4], acc[rb][cb][g * 4 + 1], acc[rb][cb][g * 4 + 2],
                            acc[rb][cb][g * 4 + 3]};
           *(f32x4 *)(base + (long long)c * ld + j) = v;
@@ -467,12 +533,12 @@ struct EpiDhPart {
 struct EpiDw {
   float *dW;
   int d, V, accumulate;
-  template <int NCB>
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][NCB], int m0, int n0, int lane,
+  template <int NRB, int NCB>
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
                                              int, char *) const {
     // One buffer resource per wave, from its first row to the end of dW: elements of
     // rows v >= V lie outside its range and the hardware drops them; lanes with
-    // j >= d get an offset outside every range.  Offsets stay below 128 * d * 4 bytes.
+    // j >= d get an offset outside every range.  Offsets stay below 32 * NRB * d * 4 bytes.
     const long long rem = (long long)(V - m0) * d * 4;
     if (rem <= 0) return;
     const int nrec = rem > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)rem;
@@ -486,7 +552,7 @@ struct EpiDw {
     }
     if (accumulate) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int roff = (rb * 32 + (i >> 2) * 8 + (i & 3)) * d * 4;
@@ -496,7 +562,7 @@ struct EpiDw {
         }
     } else {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int roff = (rb * 32 + (i >> 2) * 8 + (i & 3)) * d * 4;
@@ -529,13 +595,12 @@ struct EpiDw {
 namespace pipe {
 constexpr int OOB = (int)0x80000000;   // offset outside every buffer: reads zero
 
-// Stage geometry for a k-depth of BK bf16 (32 or 64).
-template <int BK> struct Geo {
-  static constexpr int OPB = 256 * BK * 2;   // bytes per operand per stage
-  static constexpr int STAGE = 2 * OPB;
+// Stage geometry for a k-depth of BK bf16 (32 or 64) and ROWS tile rows (256 or 384).
+template <int BK, int ROWS = 256> struct Geo {
+  static constexpr int OPB = ROWS * BK * 2;  // bytes per operand per stage
   static constexpr int ROWB = BK * 2;        // KC row bytes
   static constexpr int CPR = BK / 8;         // KC 16-B chunks per row
-  static constexpr int LOADS = BK / 2;       // 1-KB buffer loads per operand per stage
+  static constexpr int LOADS = OPB / 1024;   // 1-KB buffer loads per operand per stage
   // KC swizzle: a 16-lane LDS phase reads 16 rows of one logical chunk; rows that share
   // a 256-B bank window (same row % (256/ROWB)) get distinct chunks.
   static __device__ __forceinline__ int kc_swz(int row) {
@@ -544,47 +609,67 @@ template <int BK> struct Geo {
 };
 
 // Per-lane description of the NI chunks (of 16 B) one lane moves per operand per stage.
-template <int NI> struct LaneChunks {
-  int rel[NI];   // byte offset relative to the operand base of the stage
-  int mn[NI];    // mn offset of the chunk within the tile
-  int k[NI];     // k offset of the chunk within the stage
-};
-
-template <int KIND, int BK, int NI>
-__device__ __forceinline__ LaneChunks<NI> lane_chunks(long long ld, int w, int lane) {
-  using GG = Geo<BK>;
-  LaneChunks<NI> c;
+// Chunk j of wave w sits at LDS position q = (w*NI + j)*64 + lane (16-B units).
+//   KC: row q / CPR, 16-B column (q % CPR) ^ swz(row);
+//   MC: k row q / 32, 16-B column (q % 32) ^ ((k & 3) << 2).
+// With BK = 64 (CPR = 8) and NI even, both reduce to a part shared by all chunks of one
+// parity of j plus a wave-uniform part linear in g = w*NI + j, so a lane keeps two
+// offsets and two k (or mn) values instead of three numbers per chunk.
+template <int KIND, int BK, int NI> struct LaneChunks {
+  static_assert(BK == 64 && NI % 2 == 0, "chunk parity layout");
+  int rel[2];   // per-lane byte offset (even, odd j)
+  int var[2];   // KC: k offset; MC: mn offset (even, odd j)
+  int fix;      // KC: row within a group of 8; MC: k within a pair
+  long long ld;
+  __device__ __forceinline__ void init(long long ld_, int lane) {
+    ld = ld_;
 #pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int q = (w * NI + j) * 64 + lane;   // chunk position in LDS (16 B units)
-    if (KIND == OP_KC) {
-      const int row = q / GG::CPR, kc = (q % GG::CPR) ^ GG::kc_swz(row);
-      c.mn[j] = row;
-      c.k[j] = kc * 8;
-      c.rel[j] = (int)(((long long)row * ld + kc * 8) * 2);
-    } else {
-      const int k = q >> 5, mc = (q & 31) ^ ((k & 3) << 2);
-      c.mn[j] = mc * 8;
-      c.k[j] = k;
-      c.rel[j] = (int)(((long long)k * ld + mc * 8) * 2);
+    for (int p = 0; p < 2; ++p) {
+      if (KIND == OP_KC) {
+        // row = 8 g + (lane >> 3); swz(row) = (row >> 1) & 7 = (4 (g & 1) + (lane >> 4)) & 7
+        const int kc = (lane & 7) ^ ((4 * p + (lane >> 4)) & 7);
+        fix = lane >> 3;
+        var[p] = kc * 8;
+        rel[p] = (int)(((long long)fix * ld + kc * 8) * 2);
+      } else {
+        // k = 2 g + (lane >> 5); (k & 3) = 2 (g & 1) + (lane >> 5)
+        const int mc = (lane & 31) ^ ((2 * p + (lane >> 5)) << 2);
+        fix = lane >> 5;
+        var[p] = mc * 8;
+        rel[p] = (int)(((long long)fix * ld + mc * 8) * 2);
+      }
     }
   }
-  return c;
-}
+  // chunk g = w*NI + j of the stage: mn, k offsets within the tile / stage and the
+  // byte offset from the stage base
+  __device__ __forceinline__ void at(int g, int &mn, int &k, int &off) const {
+    const int p = g & 1;
+    if (KIND == OP_KC) {
+      mn = 8 * g + fix;
+      k = var[p];
+      off = (int)(16LL * g * ld) + rel[p];
+    } else {
+      mn = var[p];
+      k = 2 * g + fix;
+      off = (int)(4LL * g * ld) + rel[p];
+    }
+  }
+};
 
-template <int KIND, int NI> struct Loader {
-static __device__ __forceinline__ void issue(const Operand &op, const LaneChunks<NI> &c, int mn0,
-                                             int k0, char *lds, int w) {
+template <int KIND, int BK, int NI> struct Loader {
+static __device__ __forceinline__ void issue(const Operand &op, const LaneChunks<KIND, BK, NI> &c,
+                                             int mn0, int k0, char *lds, int w) {
   const unsigned short *base = (const unsigned short *)op.ptr;
   base += op_index(op, KIND, mn0, k0);   // a stage never crosses a 256-column block
   __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const bool ok = (mn0 + c.mn[j] < op.mn_ext) && (k0 + c.k[j] < op.k_ext);
+    int mn, k, off;
+    c.at(w * NI + j, mn, k, off);
+    const bool ok = (mn0 + mn < op.mn_ext) && (k0 + k < op.k_ext);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (LDS_AS void *)((LDS_AS char *)lds + (w * NI + j) * 1024), 16,
-        ok ? c.rel[j] : OOB, 0, 0, 0);
+        rs, (LDS_AS void *)((LDS_AS char *)lds + (w * NI + j) * 1024), 16, ok ? off : OOB, 0, 0, 0);
   }
 }
 };
@@ -630,28 +715,38 @@ __device__ __forceinline__ void wait_vm() {
 #define KD_SG_VMEM 0x020
 #define KD_SG_DSRD 0x100
 
-// WN = waves along n: 2 gives 4 waves of 128 x 128 (one per SIMD, 256 accumulators
-// each), 4 gives 8 waves of 128 x 64 (two per SIMD, so one wave's MFMAs cover the
-// other's waits).  NSTA / NSTB = LDS slots of the A / B rings; A may have one slot
-// more than B, giving the operand streamed from HBM one more stage of lookahead.
-template <int AK, int BKIND, class Epi, int NSTA, int NSTB, int BK, int WN>
+// WN = waves along n: 2 gives 4 waves of (TMA/2) x 128 (one per SIMD), 4 gives 8 waves
+// of (TMA/2) x 64 (two per SIMD, so one wave's MFMAs cover the other's waits).  TMA =
+// rows of the A tile: 256, or 384 for a k-contiguous A, which cuts the operand bytes
+// per flop by a sixth; with TMA = 384 the A fragments are single-buffered (each one is
+// re-read for the next substep as soon as its MFMAs have issued) so that the 192
+// accumulators per lane and the fragments fit in 256 registers.  NSTA / NSTB = LDS
+// slots of the A / B rings; A may have one slot more than B.
+template <int AK, int BKIND, class Epi, int NSTA, int NSTB, int BK, int WN, int TMA = 256>
 __global__ __attribute__((amdgpu_flat_work_group_size(128 * WN, 128 * WN),
                           amdgpu_waves_per_eu(WN / 2, WN / 2)))
 void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
   using namespace pipe;
-  using GG = Geo<BK>;
+  using GA = Geo<BK, TMA>;
+  using GB = Geo<BK, 256>;
   constexpr int NW = 2 * WN;            // waves
   constexpr int NCB = 8 / WN;           // 32-column MFMA blocks per wave
   constexpr int WNC = 32 * NCB;         // columns per wave
-  constexpr int NI = GG::LOADS / NW;    // buffer loads per wave per operand per stage
+  constexpr int WMR = TMA / 2;          // rows per wave
+  constexpr int NRB = WMR / 32;         // 32-row MFMA blocks per wave
+  constexpr int NIA = GA::LOADS / NW;   // buffer loads per wave per stage, A
+  constexpr int NIB = GB::LOADS / NW;   // buffer loads per wave per stage, B
   constexpr int S = BK / 16;            // 16-k substeps per stage
-  constexpr int LPS = 2 * NI;           // buffer loads per wave per stage
-  constexpr int NMF = 4 * NCB;          // MFMAs per wave per substep
+  constexpr int LPS = NIA + NIB;        // buffer loads per wave per stage
+  constexpr int NMF = NRB * NCB;        // MFMAs per wave per substep
+  constexpr bool FA1 = TMA > 256;       // single-buffered A fragments
   // LDS reads per substep: one per fragment, two per transposed (MC) fragment
-  constexpr int NRD = 4 * (AK == OP_MC ? 2 : 1) + NCB * (BKIND == OP_MC ? 2 : 1);
+  constexpr int NRD = NRB * (AK == OP_MC ? 2 : 1) + NCB * (BKIND == OP_MC ? 2 : 1);
   static_assert(NSTB >= 2 && (NSTA == NSTB || NSTA == NSTB + 1), "ring shapes");
-  __shared__ __attribute__((aligned(1024))) char smem[(NSTA + NSTB) * GG::OPB];
-  char *const smemB = smem + NSTA * GG::OPB;
+  static_assert(TMA == 256 || (TMA == 384 && AK == OP_KC), "a 384-row A tile must be k-contiguous");
+  static_assert(GA::LOADS % NW == 0 && GB::LOADS % NW == 0, "whole loads per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[NSTA * GA::OPB + NSTB * GB::OPB];
+  char *const smemB = smem + NSTA * GA::OPB;
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per_split = G.ntm * G.ntn;
@@ -665,7 +760,7 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
     tn = rem / G.ntm;
     tm = rem - tn * G.ntm;
   }
-  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int m0 = tm * TMA, n0 = tn * kTile;
   const int kb = split * G.k_len;
   const int ke = min(G.k_total, kb + G.k_len);
   const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
@@ -673,16 +768,18 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wr = w / WN, wc = w % WN;
-  const LaneChunks<NI> ca = lane_chunks<AK, BK, NI>(A.ld, w, lane);
-  const LaneChunks<NI> cb = lane_chunks<BKIND, BK, NI>(B.ld, w, lane);
+  LaneChunks<AK, BK, NIA> ca;
+  LaneChunks<BKIND, BK, NIB> cb;
+  ca.init(A.ld, lane);
+  cb.init(B.ld, lane);
   // k beyond this split's range reads zero (and moves no data)
   Operand Ak = A, Bk = B;
   Ak.k_ext = min(A.k_ext, ke);
   Bk.k_ext = min(B.k_ext, ke);
 
-  f32x16 acc[4][NCB];
+  f32x16 acc[NRB][NCB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NRB; ++i)
 #pragma unroll
     for (int j = 0; j < NCB; ++j) acc[i][j] = f32x16{};
 
@@ -690,15 +787,16 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
   // are all-zero loads, so the count of loads in flight is the same in every
   // iteration); then stage 0 landed.
   for (int s = 0; s < NSTA; ++s) {
-    Loader<AK, NI>::issue(Ak, ca, m0, kb + s * BK, smem + s * GG::OPB, w);
-    if (s < NSTB) Loader<BKIND, NI>::issue(Bk, cb, n0, kb + s * BK, smemB + s * GG::OPB, w);
+    Loader<AK, BK, NIA>::issue(Ak, ca, m0, kb + s * BK, smem + s * GA::OPB, w);
+    if (s < NSTB) Loader<BKIND, BK, NIB>::issue(Bk, cb, n0, kb + s * BK, smemB + s * GB::OPB, w);
   }
-  wait_vm<NI * (NSTA + NSTB - 2), false>();
+  wait_vm<NIA * (NSTA - 1) + NIB * (NSTB - 1), false>();
   __syncthreads();
 
-  bf16x8 fa[2][4], fb[2][NCB];
+  constexpr int NFA = FA1 ? 1 : 2;
+  bf16x8 fa[NFA][NRB], fb[2][NCB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa[0][i] = PFrag<AK, BK>::load(smem, wr * 128 + i * 32, 0, lane);
+  for (int i = 0; i < NRB; ++i) fa[0][i] = PFrag<AK, BK>::load(smem, wr * WMR + i * 32, 0, lane);
 #pragma unroll
   for (int j = 0; j < NCB; ++j) fb[0][j] = PFrag<BKIND, BK>::load(smemB, wc * WNC + j * 32, 0, lane);
 
@@ -706,21 +804,30 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
   for (int it = 0; it < nk; ++it) {
     const int anext = acur + 1 == NSTA ? 0 : acur + 1;
     const int bnext = bcur + 1 == NSTB ? 0 : bcur + 1;
-    char *cura = smem + acur * GG::OPB;
-    char *curb = smemB + bcur * GG::OPB;
+    char *cura = smem + acur * GA::OPB;
+    char *curb = smemB + bcur * GB::OPB;
 #pragma unroll
     for (int ss = 0; ss < S - 1; ++ss) {
       // substep ss on registers [ss&1]; read substep ss+1 meanwhile
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[(ss + 1) & 1][i] = PFrag<AK, BK>::load(cura, wr * 128 + i * 32, ss + 1, lane);
-#pragma unroll
       for (int j = 0; j < NCB; ++j)
         fb[(ss + 1) & 1][j] = PFrag<BKIND, BK>::load(curb, wc * WNC + j * 32, ss + 1, lane);
+      if constexpr (FA1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NRB; ++i) {
 #pragma unroll
-        for (int j = 0; j < NCB; ++j) acc[i][j] = mma(fa[ss & 1][i], fb[ss & 1][j], acc[i][j]);
+          for (int j = 0; j < NCB; ++j) acc[i][j] = mma(fa[0][i], fb[ss & 1][j], acc[i][j]);
+          fa[0][i] = PFrag<AK, BK>::load(cura, wr * WMR + i * 32, ss + 1, lane);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NRB; ++i)
+          fa[(ss + 1) & 1][i] = PFrag<AK, BK>::load(cura, wr * WMR + i * 32, ss + 1, lane);
+#pragma unroll
+        for (int i = 0; i < NRB; ++i)
+#pragma unroll
+          for (int j = 0; j < NCB; ++j) acc[i][j] = mma(fa[ss & 1][i], fb[ss & 1][j], acc[i][j]);
+      }
       // one or two LDS reads in the shadow of each MFMA
 #pragma unroll
       for (int q = 0; q < NMF; ++q) {
@@ -734,25 +841,36 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
     // stage it in registers or accumulators, since its slots are refilled next.  Loads
     // are issued B(j+NSTB) then A(j+NSTA) in iteration j, so what may still be in
     // flight here is A(it+2) when A has the extra slot, else nothing.
-    wait_vm<NI * (NSTA - NSTB), true>();
+    wait_vm<NIA * (NSTA - NSTB), true>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
     // last substep on registers [(S-1)&1]; meanwhile read substep 0 of stage it+1 and
     // refill this stage's slots with B(it+NSTB) and A(it+NSTA)
-    const char *nxa = smem + anext * GG::OPB;
-    const char *nxb = smemB + bnext * GG::OPB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = PFrag<AK, BK>::load(nxa, wr * 128 + i * 32, 0, lane);
+    const char *nxa = smem + anext * GA::OPB;
+    const char *nxb = smemB + bnext * GB::OPB;
 #pragma unroll
     for (int j = 0; j < NCB; ++j) fb[0][j] = PFrag<BKIND, BK>::load(nxb, wc * WNC + j * 32, 0, lane);
-    Loader<BKIND, NI>::issue(Bk, cb, n0, kb + (it + NSTB) * BK, curb, w);
-    Loader<AK, NI>::issue(Ak, ca, m0, kb + (it + NSTA) * BK, cura, w);
+    if constexpr (FA1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NRB; ++i) {
 #pragma unroll
-      for (int j = 0; j < NCB; ++j)
-        acc[i][j] = mma(fa[(S - 1) & 1][i], fb[(S - 1) & 1][j], acc[i][j]);
+        for (int j = 0; j < NCB; ++j) acc[i][j] = mma(fa[0][i], fb[(S - 1) & 1][j], acc[i][j]);
+        fa[0][i] = PFrag<AK, BK>::load(nxa, wr * WMR + i * 32, 0, lane);
+      }
+      Loader<BKIND, BK, NIB>::issue(Bk, cb, n0, kb + (it + NSTB) * BK, curb, w);
+      Loader<AK, BK, NIA>::issue(Ak, ca, m0, kb + (it + NSTA) * BK, cura, w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NRB; ++i) fa[0][i] = PFrag<AK, BK>::load(nxa, wr * WMR + i * 32, 0, lane);
+      Loader<BKIND, BK, NIB>::issue(Bk, cb, n0, kb + (it + NSTB) * BK, curb, w);
+      Loader<AK, BK, NIA>::issue(Ak, ca, m0, kb + (it + NSTA) * BK, cura, w);
+#pragma unroll
+      for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int j = 0; j < NCB; ++j)
+          acc[i][j] = mma(fa[(S - 1) & 1][i], fb[(S - 1) & 1][j], acc[i][j]);
+    }
     // reads for the next stage in the first half of the MFMAs (they gate the next
     // iteration), loads in the second half
 #pragma unroll
@@ -771,7 +889,7 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
     bcur = bnext;
   }
   wait_vm<0, false>();  // the zero loads issued past the end
-  epi(acc, m0 + wr * 128, n0 + wc * WNC, lane, split, smem);
+  epi(acc, m0 + wr * WMR, n0 + wc * WNC, lane, split, smem);
 }
 
 template <int DT, int AK, int BKIND, class Epi>
@@ -797,26 +915,109 @@ static inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b)
 // ---------------------------------------------------------------------------------
 hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
                            int64_t V, float2 *partials, int64_t ld_part, const int *boff,
-                           const unsigned *bent, float *zg, int32_t K, hipStream_t s) {
+                           const unsigned *bent, float *zg, int32_t K, void *u, int64_t V_pad,
+                           int64_t C_alloc, hipStream_t s) {
   Operand A{W, d, (int)V, (int)d, 256};
   Operand B{h_c, d, (int)rows, (int)d, 256};
   GemmGrid G{cdiv(V, kTile), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
-  EpiFwdLse e{partials, ld_part, (int)V, (int)rows, boff, bent, G.ntn, zg, (int)K};
-  return dtype == 1 ? run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s)
-                    : run_gemm<0, OP_KC, OP_KC>(A, B, G, e, s);
+  if (dtype == 1) {
+    EpiFwdLse<1> e{partials, ld_part, (int)V, (int)rows, boff, bent, G.ntn, zg, (int)K, u,
+                   C_alloc * 256, (int)V_pad};
+    return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
+  }
+  EpiFwdLse<0> e{partials, ld_part, (int)V, (int)rows, boff, bent, G.ntn, zg, (int)K, u,
+                 C_alloc * 256, (int)V_pad};
+  return run_gemm<0, OP_KC, OP_KC>(A, B, G, e, s);
+}
+
+// Single-sweep backward: u = exp(z - m_g) from the forward epilogue (m_g the max of the
+// token's 128-row group g) becomes dz = sM * exp(z - lse) = sM * exp(m_g - lse) * u, in
+// place; bf16 also writes dzT (token-contiguous, zeros for tokens rows <= c < C_alloc).
+// A block takes 64 vocabulary rows (one group) x 64 tokens and transposes through LDS.
+template <int DT>
+__global__ __launch_bounds__(256) void k_rescale_dz(void *dz, long long ts, unsigned short *dzt,
+                                                    long long ldt, const float2 *part,
+                                                    long long ld, const float *lse,
+                                                    const float *sM, int rows, int V) {
+  __shared__ float f[64];
+  __shared__ __attribute__((aligned(16))) unsigned short t[64][72];
+  const int v0 = blockIdx.x * 64, c0 = blockIdx.y * 64, tid = threadIdx.x;
+  if (tid < 64) {
+    const int c = c0 + tid;
+    float fc = 0.f;
+    if (c < rows && v0 < V)
+      fc = sM[c] * fast_exp2((part[(long long)(v0 / kLseRows) * ld + c].x - lse[c]) * kLog2e);
+    f[tid] = fc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = tid; q < 512; q += 256) {
+    const int r = q >> 3, v8 = (q & 7) * 8;
+    const int c = c0 + r, v = v0 + v8;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (c < rows) {
+      const float a = f[r];
+      const long long o = (long long)(v >> 8) * ts + c * 256 + (v & 255);
+      if (DT == 1) {
+        u32x4 *pp = (u32x4 *)((unsigned short *)dz + o);
+        const u32x4 in = *pp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          val[e] = pack_bf16x2(a * bf16_to_f32((unsigned short)(in[e] & 0xFFFFu)),
+                               a * bf16_to_f32((unsigned short)(in[e] >> 16)));
+        *pp = val;
+      } else {
+        f32x4 *pp = (f32x4 *)((float *)dz + o);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 x = pp[h];
+          pp[h] = f32x4{a * x[0], a * x[1], a * x[2], a * x[3]};
+        }
+      }
+    }
+    if (DT == 1) *(u32x4 *)&t[r][v8] = val;
+  }
+  if (DT == 0) return;
+  __syncthreads();
+#pragma unroll
+  for (int q = tid; q < 512; q += 256) {
+    const int vr = q >> 3, c8 = (q & 7) * 8;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (unsigned)t[c8 + 2 * e][vr] | ((unsigned)t[c8 + 2 * e + 1][vr] << 16);
+    *(u32x4 *)(dzt + (long long)(v0 + vr) * ldt + c0 + c8) = o;
+  }
+}
+
+hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, const float2 *partials,
+                             const float *lse, const float *sM, int64_t rows, int64_t V,
+                             int64_t V_pad, int64_t C_alloc, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(V_pad / 64), (unsigned)(C_alloc / 64));
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_rescale_dz<1>, grid, dim3(256), 0, s, dz, (long long)C_alloc * 256,
+                       (unsigned short *)dzt, (long long)C_alloc, partials, (long long)C_alloc,
+                       lse, sM, (int)rows, (int)V);
+  else
+    hipLaunchKernelGGL(k_rescale_dz<0>, grid, dim3(256), 0, s, dz, (long long)C_alloc * 256,
+                       (unsigned short *)nullptr, 0LL, partials, (long long)C_alloc, lse, sM,
+                       (int)rows, (int)V);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
-                           int64_t V, const float *lse, const float *sM, void *dz,
+                           int64_t V, const float *lse, const float *sM, void *dz, void *dzt,
                            int64_t V_pad, int64_t C_alloc, hipStream_t s) {
   Operand A{W, d, (int)V, (int)d, 256};
   Operand B{h_c, d, (int)rows, (int)d, 256};
   GemmGrid G{cdiv(V, kTile), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
   if (dtype == 1) {
-    EpiBwdDz<1> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows};
+    EpiBwdDz<1> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows, (int)V_pad,
+                  (unsigned short *)dzt, C_alloc};
     return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
   }
-  EpiBwdDz<0> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows};
+  EpiBwdDz<0> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows, (int)V_pad, nullptr, 0};
   return run_gemm<0, OP_KC, OP_KC>(A, B, G, e, s);
 }
 
@@ -874,16 +1075,58 @@ hipError_t launch_transpose_w(const void *W, int64_t V, int64_t d, int64_t V_pad
   return hipGetLastError();
 }
 
-hipError_t launch_dw_gemm(int dtype, const void *dz, const void *h_c, int64_t rows, int64_t d,
-                          int64_t V, int64_t V_pad, int64_t C_alloc, float *dW, int accumulate,
-                          hipStream_t s) {
-  // D[v][j] = sum_c dz[c][v] h[c][j]: A = dz as MC ([c][v]), B = h as MC ([c][j]).
-  Operand A{dz, 256, (int)V_pad, (int)rows, C_alloc * 256};
-  Operand B{h_c, d, (int)d, (int)rows, 256};
+hipError_t launch_dw_gemm(int dtype, const void *dz, const void *dzt, const void *h_c,
+                          const void *ht, int64_t rows, int64_t d, int64_t V, int64_t V_pad,
+                          int64_t C_alloc, float *dW, int accumulate, hipStream_t s) {
+  // D[v][j] = sum_c dz[c][v] h[c][j]
   GemmGrid G{cdiv(V, kTile), cdiv(d, kTile), 1, (int)rows, (int)rows, 0};
   EpiDw e{dW, (int)d, (int)V, accumulate};
-  return dtype == 1 ? run_gemm<1, OP_MC, OP_MC>(A, B, G, e, s)
-                    : run_gemm<0, OP_MC, OP_MC>(A, B, G, e, s);
+  if (dtype == 1) {
+    // A = dzT ([v][c]), B = hT ([j][c]): both token-contiguous (KC)
+    Operand A{dzt, C_alloc, (int)V, (int)rows, 256};
+    Operand B{ht, C_alloc, (int)d, (int)rows, 256};
+    return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
+  }
+  // A = dz as MC ([c][v] in 256-column blocks), B = h as MC ([c][j])
+  Operand A{dz, 256, (int)V_pad, (int)rows, C_alloc * 256};
+  Operand B{h_c, d, (int)d, (int)rows, 256};
+  return run_gemm<0, OP_MC, OP_MC>(A, B, G, e, s);
+}
+
+// h chunk [rows][d] -> hT [d][ldt] (bf16), through a 64 x 64 LDS tile.
+__global__ __launch_bounds__(256) void k_transpose_h(const unsigned short *h, int rows, int d,
+                                                     long long ldt, unsigned short *ht) {
+  __shared__ __attribute__((aligned(16))) unsigned short t[64][72];
+  const int c0 = blockIdx.x * 64, j0 = blockIdx.y * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int q = tid; q < 512; q += 256) {
+    const int r = q >> 3, j8 = (q & 7) * 8;
+    const int c = c0 + r, j = j0 + j8;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (c < rows && j < d) val = *(const u32x4 *)(h + (long long)c * d + j);  // d % 8 == 0
+    *(u32x4 *)&t[r][j8] = val;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = tid; q < 512; q += 256) {
+    const int jr = q >> 3, c8 = (q & 7) * 8;
+    const int j = j0 + jr, c = c0 + c8;
+    if (j >= d || c >= rows) continue;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (unsigned)t[c8 + 2 * e][jr] | ((unsigned)t[c8 + 2 * e + 1][jr] << 16);
+    *(u32x4 *)(ht + (long long)j * ldt + c) = o;  // ldt % 8 == 0: columns up to c+7 < ldt
+  }
+}
+
+hipError_t launch_transpose_h(const void *h_c, int64_t rows, int64_t d, int64_t C_alloc, void *ht,
+                              hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((d + 63) / 64));
+  hipLaunchKernelGGL(k_transpose_h, grid, dim3(256), 0, s, (const unsigned short *)h_c, (int)rows,
+                     (int)d, (long long)C_alloc, (unsigned short *)ht);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------
@@ -1206,7 +1449,8 @@ hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStr
 // probabilities of its later duplicates in order and does the update, so no two
 // threads touch the same element.
 template <int DT>
-__global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, const int32_t *idx,
+__global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigned short *dzt,
+                                                 long long ldt, const int32_t *idx,
                                                  const float *p, const float *srow, int rows,
                                                  int K) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1239,7 +1483,9 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, const i
     if (!first) continue;
     if (DT == 1) {
       unsigned short *q = (unsigned short *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
-      *q = f32_to_bf16(bf16_to_f32(*q) - sr * tot);
+      const unsigned short nv = f32_to_bf16(bf16_to_f32(*q) - sr * tot);
+      *q = nv;
+      dzt[(long long)v * ldt + r] = nv;
     } else {
       float *q = (float *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
       *q = *q - sr * tot;
@@ -1247,16 +1493,17 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, const i
   }
 }
 
-hipError_t launch_scatter(int dtype, void *dz, int64_t C_alloc, const int32_t *idx_c,
+hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t C_alloc, const int32_t *idx_c,
                           const float *p_c, const float *srow, int64_t rows, int32_t K,
                           hipStream_t s) {
   const int blocks = (int)((rows + 3) / 4);
   if (dtype == 1)
-    hipLaunchKernelGGL(k_scatter<1>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256, idx_c,
-                       p_c, srow, (int)rows, (int)K);
+    hipLaunchKernelGGL(k_scatter<1>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256,
+                       (unsigned short *)dzt, (long long)C_alloc, idx_c, p_c, srow, (int)rows,
+                       (int)K);
   else
-    hipLaunchKernelGGL(k_scatter<0>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256, idx_c,
-                       p_c, srow, (int)rows, (int)K);
+    hipLaunchKernelGGL(k_scatter<0>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256,
+                       (unsigned short *)nullptr, 0LL, idx_c, p_c, srow, (int)rows, (int)K);
   return hipGetLastError();
 }
 

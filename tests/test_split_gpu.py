@@ -1,7 +1,9 @@
 """The forward and backward halves (kd_chunked_kl_fwd / kd_chunked_kl_bwd) through the C
-ABI: with an upstream gradient of 1 they reproduce the fused call bit for bit, an
-upstream gradient g scales dh and dW, the autograd wrapper gives the oracle's
-gradients, and the edge cases behave as in the fused call."""
+ABI: with an upstream gradient of 1 they reproduce the fused call's forward outputs bit
+for bit and its gradients to rounding (the backward half recomputes the logits; the
+fused call keeps each chunk's exp(z - max) from its forward), an upstream gradient g
+scales dh and dW, the autograd wrapper gives the oracle's gradients, and the edge cases
+behave as in the fused call."""
 import numpy as np
 import pytest
 
@@ -37,26 +39,36 @@ def _bits(t, torch):
     return t.detach().contiguous().view(torch.uint8).cpu().numpy()
 
 
+def _same_as_fused(a, b, dtype, torch, fwd_keys):
+    for k in fwd_keys:
+        assert np.array_equal(_bits(a[k], torch), _bits(b[k], torch)), k
+    for k in ["dh", "dW"]:
+        ga, gb = to_f64(a[k], torch), to_f64(b[k], torch)
+        assert grad_err(dtype, ga, gb) <= TOL[dtype]["grad"], k
+    # rows of masked tokens are exactly zero in both
+    za, zb = np.all(to_f64(a["dh"], torch) == 0, axis=1), np.all(to_f64(b["dh"], torch) == 0, axis=1)
+    assert np.array_equal(za, zb)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_split_equals_fused_bitwise(torch_cuda, dtype):
+def test_split_matches_fused(torch_cuda, dtype):
     """Ragged shapes (V, d, N off the tile grid, partial last chunk), masked rows and a
-    repeated index: fwd + bwd(g = 1) give the fused call's outputs bit for bit."""
+    repeated index: fwd + bwd(g = 1) give the fused call's forward outputs bit for bit
+    and its gradients within the gradient tolerance."""
     torch = torch_cuda
     inp = synth.make(1, seed=91, N=700, d=264, V=3001, K=7, chunk=300, dtype=dtype)
     inp.mask[[0, 5, 299, 300, 699]] = 0
     inp.idx[3, 1] = inp.idx[3, 0]
     a, b = _split(inp, torch), _fused(inp, torch)
-    for k in ["loss", "row_lse", "row_loss", "zg", "dh", "dW"]:
-        assert np.array_equal(_bits(a[k], torch), _bits(b[k], torch)), k
+    _same_as_fused(a, b, dtype, torch, ["loss", "row_lse", "row_loss", "zg"])
 
 
-def test_split_equals_fused_bitwise_full_size(torch_cuda):
+def test_split_matches_fused_full_size(torch_cuda):
     """The 4096-token, V = 128256 workload in the benchmark's launch configuration."""
     torch = torch_cuda
     inp = synth.make(1)
     a, b = _split(inp, torch), _fused(inp, torch)
-    for k in ["loss", "row_lse", "dh", "dW"]:
-        assert np.array_equal(_bits(a[k], torch), _bits(b[k], torch)), k
+    _same_as_fused(a, b, "bf16", torch, ["loss", "row_lse"])
 
 
 def test_split_against_oracle_with_upstream_gradient(torch_cuda):
