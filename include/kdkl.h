@@ -85,7 +85,7 @@ int kd_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk
  *   row_lse   [N]     float32         optional: lse[n]                 (NULL = skip)
  *   zg        [N, K]  float32         optional: z[n, idx[n,k]]         (NULL = skip)
  *   workspace         >= kd_workspace_bytes(...) bytes, 256-byte aligned
- * Sizes: N >= 0, 1 <= K <= 65536, V >= 1, d >= 8 with d % 8 == 0, chunk >= 1,
+ * Sizes: N >= 0, 1 <= K <= 32768, V >= 1, d >= 8 with d % 8 == 0, chunk >= 1,
  *   d <= 2^20, V <= 2^24, N*d and N*K below 2^62.  N == 0 writes loss = 0 and dW = 0.
  * chunk is the number of token rows whose logits are live at once; the last
  *   chunk may be partial; results do not depend on it beyond float rounding.

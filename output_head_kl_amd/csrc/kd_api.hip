@@ -66,7 +66,7 @@ int check_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32
   if (N < 0) return fail(KD_E_ARG, "N = %lld < 0", (long long)N);
   if (d < 1 || V < 1 || K < 1) return fail(KD_E_ARG, "d, V and K must be >= 1");
   if (chunk < 1) return fail(KD_E_ARG, "chunk = %lld < 1", (long long)chunk);
-  if (K > 65536) return fail(KD_E_UNSUPPORTED, "K = %d above 65536", K);
+  if (K > 32768) return fail(KD_E_UNSUPPORTED, "K = %d above 32768", K);
   if (d % 8 != 0) return fail(KD_E_UNSUPPORTED, "d = %lld is not a multiple of 8", (long long)d);
   if (d > (1 << 20) || V > ((int64_t)1 << 24))
     return fail(KD_E_UNSUPPORTED, "d or V too large");
@@ -103,12 +103,15 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   const int64_t Nn = N > 0 ? N : 1;
   L->C = chunk < Nn ? chunk : Nn;
   L->C_alloc = rup(L->C, kTile);
-  L->V_pad = rup(V, kTile);
+  L->tv = tile_rows(dtype);
+  L->V_pad = rup(V, L->tv == kTile ? kTile : 3 * kTile);  // a multiple of 256 and of tv
   L->d_pad = rup(d, kTile);
-  L->n_lse = (V + kLseRows - 1) / kLseRows;
-  // Split the vocabulary of the dh GEMM so that about three workgroups per CU run.
-  const int64_t tiles = (L->d_pad / kTile) * (L->C_alloc / kTile);
-  int64_t ns = (768 + tiles - 1) / tiles;
+  L->n_lse = (V + L->tv / 2 - 1) / (L->tv / 2);
+  // Split the vocabulary of the dh GEMM so that two (bf16) or three (fp32) workgroups
+  // per CU run.
+  const int64_t tiles = ((d + L->tv - 1) / L->tv) * (L->C_alloc / kTile);
+  const int64_t target = dtype == KD_BF16 ? 512 : 768;
+  int64_t ns = (target + tiles - 1) / tiles;
   const int64_t max_by_k = L->V_pad / kTile;  // at least one dz column block per split
   if (ns > max_by_k) ns = max_by_k;
   if (ns > 16) ns = 16;
@@ -131,7 +134,7 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->off_zg = take((size_t)L->C_alloc * K * 4);
   L->off_dz = take((size_t)L->C_alloc * L->V_pad * es);
   L->off_dhpart = take((size_t)L->nsplit * L->C_alloc * L->d_pad * 4);
-  L->nkeys = (V + kTile - 1) / kTile * (L->C_alloc / kTile);
+  L->nkeys = L->V_pad / L->tv * (L->C_alloc / kTile);
   L->off_bcount = take((size_t)L->nkeys * 4);
   L->off_bcursor = take((size_t)L->nkeys * 4);
   L->off_boff = take((size_t)(L->nkeys + 1) * 4);
@@ -303,7 +306,8 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
 
     if (fwd) {
       LAUNCH(kd::KC_BUCKET,
-             kd::launch_buckets(idx_k, rows, K, V, bcount, bcursor, boff, bent, stream));
+             kd::launch_buckets(idx_k, rows, K, L.tv, (int)(L.V_pad / L.tv), bcount, bcursor,
+                                boff, bent, stream));
       // the fused call keeps this chunk's exp(z - max) for its backward (no recompute)
       void *u = (mode == M_FUSED && count > 0) ? dz : nullptr;
       LAUNCH(kd::KC_FWD_GEMM, kd::launch_fwd_gemm(dtype, W, h_c, rows, d, V, partials, L.C_alloc,

@@ -8,10 +8,14 @@
 
 namespace kd {
 
-// Output tile of every GEMM launch: 256 x 256, four waves of 128 x 128.
+// Output tile along tokens (and along everything in fp32): 256.
 constexpr int kTile = 256;
-// Vocabulary rows per (max, sum-exp) partial written by the forward GEMM (one wave's rows).
-constexpr int kLseRows = 128;
+// Rows of the A tile of the bf16 GEMMs (vocabulary entries, or hidden units in dh):
+// 384, in two wave rows of 192; fp32 keeps 256 (two wave rows of 128).  The forward
+// GEMM writes one (max, sum-exp) partial per wave row, i.e. per tile_rows / 2
+// vocabulary entries.
+constexpr int kTileA16 = 384;
+inline int tile_rows(int dtype) { return dtype == 1 ? kTileA16 : kTile; }
 
 // Kernel classes for timing (kd_profile_*).
 enum KClass {
@@ -35,12 +39,13 @@ enum KClass {
 struct Layout {
   int64_t C;          // token rows per chunk (min(chunk, N))
   int64_t C_alloc;    // C rounded up to the tile
-  int64_t V_pad;      // V rounded up to the tile (dz holds V_pad / 256 column blocks)
+  int tv;             // tile_rows(dtype)
+  int64_t V_pad;      // V rounded up to 256 and to tv (dz holds V_pad / 256 column blocks)
   int64_t d_pad;      // d rounded up to the tile (row pitch of the dh partials)
-  int64_t n_lse;      // ceil(V / kLseRows)
+  int64_t n_lse;      // ceil(V / (tv / 2))
   int nsplit;         // vocabulary splits of the dh GEMM
   int64_t k_split;    // vocabulary rows per split (a multiple of 256)
-  int64_t nkeys;      // buckets per chunk: ceil(V / 256) * C_alloc / 256
+  int64_t nkeys;      // buckets per chunk: V_pad / tv * C_alloc / 256
   size_t off_flags, off_acc, off_partials, off_lse, off_sM, off_s, off_rowterm, off_zg,
       off_dz, off_dhpart, off_bcount, off_bcursor, off_boff, off_bent, off_wt, off_idxloc,
       off_dzt, off_ht, total;
@@ -54,11 +59,13 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_validate(const int32_t *idx, const float *p, int64_t NK, int64_t V,
                            const uint8_t *mask, int64_t N, int *flags,
                            unsigned long long *count, hipStream_t s);
-// Teacher hits of a chunk sorted by 256 x 256 output tile: offsets[key..key+1) of
-// entries (c_local | v_local << 8 | k << 16), key = (v / 256) * ceil(rows / 256) + c / 256.
-// counts must be zero on entry and are left zero.
-hipError_t launch_buckets(const int32_t *idx_c, int64_t rows, int32_t K, int64_t V, int *counts,
-                          int *cursor, int *offsets, unsigned *entries, hipStream_t s);
+// Teacher hits of a chunk sorted by tv x 256 output tile of the logits GEMM: offsets
+// [key..key+1) of entries (c % 256 | (v % tv) << 8 | k << 17), key = (v / tv) *
+// ceil(rows / 256) + c / 256, for ntv = V_pad / tv vocabulary tiles.  counts must be
+// zero on entry and are left zero.
+hipError_t launch_buckets(const int32_t *idx_c, int64_t rows, int32_t K, int tv, int ntv,
+                          int *counts, int *cursor, int *offsets, unsigned *entries,
+                          hipStream_t s);
 // Logits GEMM with the per-tile (max, sum exp) epilogue and the fused gather into zg;
 // with u non-null it also writes u = exp(z - max of the token's 128-row group) into the
 // dz buffer (rows v < V_pad, tokens c < rows) for launch_rescale_dz.

@@ -310,17 +310,19 @@ void gemm_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
 // ---------------------------------------------------------------------------------
 // Epilogues
 // ---------------------------------------------------------------------------------
-// Forward: tile rows are vocabulary entries v, columns are tokens c.  Each lane holds
-// 64 of a token's 128 values in the wave's square; lane l^32 holds the rest.
-//  * per (token, 128 vocabulary rows): max and sum of exp(z - max) -> part;
+// Forward: tile rows are vocabulary entries v, columns are tokens c.  A wave holds
+// WR = 32 * NRB rows (128, or 192 in the 384-row bf16 tile) of each of its tokens: each
+// lane half of them, lane l^32 the rest.
+//  * per (token, WR vocabulary rows): max and sum of exp(z - max) -> part, at index
+//    (first row of the wave) / WR;
 //  * gather: the tile's teacher hits (bucket key = vocabulary tile * token tiles + token
-//    tile, entries packed c_local | v_local << 8 | k << 16) read z from the tile, staged
-//    through LDS in four slices of 64 vocabulary rows ([256 tokens][68] fp32, 68 KB);
+//    tile, entries packed c_local | v_local << 8 | k << 17) read z from the tile, staged
+//    through LDS in slices of 64 vocabulary rows ([256 tokens][68] fp32, 68 KB);
 //  * optionally (u != null) u = exp(z - max) itself, in dz's layout, for the single-sweep
 //    backward (k_rescale_dz turns it into dz once the logsumexp is known).
 template <int DT>
 struct EpiFwdLse {
-  float2 *part;   // [n_lse][ld] (max, sum exp(z - max)) per 128 vocabulary rows
+  float2 *part;   // [n_lse][ld] (max, sum exp(z - max)) per wave row of the tile
   long long ld;
   int V, rows;
   const int *boff;        // bucket offsets, [ntm * ntn + 1]
@@ -334,15 +336,54 @@ struct EpiFwdLse {
   template <int NRB, int NCB>
   __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
                                              int, char *smem) const {
-    static_assert(NRB == 4, "one (max, sum) partial per 128 vocabulary rows");
+    constexpr int WR = 32 * NRB, TR = 2 * WR, SPW = WR / 64;  // slices of 64 rows per wave row
+    // Fused gather first, while no other temporaries are live (the same branch for every
+    // wave of the workgroup).
+    const int tm = m0 / TR, tn = n0 >> 8;
+    const int key = tm * ntn + tn;
+    const int beg = boff[key], end = boff[key + 1];
+    if (beg != end) {
+      const int t = threadIdx.x, wr = (m0 - tm * TR) / WR;
+      constexpr int P = 68;
+      const int cl0 = (n0 & 255) + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 2 * SPW; ++q) {
+        __syncthreads();
+        if (wr == q / SPW) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int rb = (q % SPW) * 2 + h;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int vloc = h * 32 + g * 8 + (lane >> 5) * 4;
+                const f32x4 v4 = {acc[rb][cb][g * 4], acc[rb][cb][g * 4 + 1], acc[rb][cb][g * 4 + 2],
+                                  acc[rb][cb][g * 4 + 3]};
+                *(LDS_AS f32x4 *)((LDS_AS char *)smem + ((cl0 + cb * 32) * P + vloc) * 4) = v4;
+              }
+          }
+        }
+        __syncthreads();
+        for (int e = beg + t; e < end; e += blockDim.x) {
+          const unsigned ent = bent[e];
+          const int cl = ent & 255, vloc = (ent >> 8) & 511, k = ent >> 17;
+          if ((vloc >> 6) == q)
+            zg[(long long)(tn * 256 + cl) * K + k] =
+                *(const LDS_AS float *)((const LDS_AS char *)smem + (cl * P + (vloc & 63)) * 4);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (max, sum exp) per wave row and token, and u
+    const int vl = m0 + (lane >> 5) * 4;
     if (m0 < V) {
-      const bool full = m0 + 128 <= V;
-      const int vl = m0 + (lane >> 5) * 4;
+      const bool full = m0 + WR <= V;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
@@ -354,7 +395,7 @@ struct EpiFwdLse {
         const bool keep = u != nullptr && c < rows;
         float s = 0.f;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int v0 = vl + rb * 32 + g * 8;
@@ -377,19 +418,19 @@ struct EpiFwdLse {
             }
           }
         s = halves_sum(s);
-        if (lane < 32 && c < rows) part[(long long)(m0 / kLseRows) * ld + c] = make_float2(mx, s);
+        if (lane < 32 && c < rows) part[(long long)(m0 / WR) * ld + c] = make_float2(mx, s);
       }
     } else if (u != nullptr) {
-      // rows V <= v < V_pad of a tile wholly past V: u = 0
+      // rows V <= v < V_pad of a wave wholly past V: u = 0
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const int c = n0 + cb * 32 + (lane & 31);
         if (c >= rows) continue;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int v0 = m0 + (lane >> 5) * 4 + rb * 32 + g * 8;
+            const int v0 = vl + rb * 32 + g * 8;
             if (v0 >= V_pad) continue;
             if (DT == 1)
               *(u32x2 *)((unsigned short *)u + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) =
@@ -398,41 +439,6 @@ struct EpiFwdLse {
               *(f32x4 *)((float *)u + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) =
                   f32x4{0.f, 0.f, 0.f, 0.f};
           }
-      }
-    }
-    // fused gather (the same branch for every wave of the workgroup)
-    const int tm = m0 >> 8, tn = n0 >> 8;
-    const int key = tm * ntn + tn;
-    const int beg = boff[key], end = boff[key + 1];
-    if (beg == end) return;
-    const int t = threadIdx.x, wr = (m0 & 255) >> 7;
-    constexpr int P = 68;
-    const int cl0 = (n0 & 255) + (lane & 31);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __syncthreads();
-      if (wr == (q >> 1)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int rb = (q & 1) * 2 + h;
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int vloc = h * 32 + g * 8 + (lane >> 5) * 4;
-              const f32x4 v4 = {acc[rb][cb][g * 4], acc[rb][cb][g * 4 + 1], acc[rb][cb][g * 4 + 2],
-                                acc[rb][cb][g * 4 + 3]};
-              *(LDS_AS f32x4 *)((LDS_AS char *)smem + ((cl0 + cb * 32) * P + vloc) * 4) = v4;
-            }
-        }
-      }
-      __syncthreads();
-      for (int e = beg + t; e < end; e += blockDim.x) {
-        const unsigned ent = bent[e];
-        const int cl = ent & 255, vloc = (ent >> 8) & 255, k = ent >> 16;
-        if ((vloc >> 6) == q)
-          zg[(long long)(tn * 256 + cl) * K + k] =
-              *(const LDS_AS float *)((const LDS_AS char *)smem + (cl * P + (vloc & 63)) * 4);
       }
     }
   }
@@ -900,8 +906,8 @@ static hipError_t run_gemm(const Operand &A, const Operand &B, const GemmGrid &G
   // 8 waves (two per SIMD), two LDS stages of 64 k: a KC operand row is then one
   // 128-byte segment per stage, which halves the memory requests of k-contiguous operands
   if constexpr (DT == 1)
-    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKIND, Epi, 2, 2, 64, 4>), dim3((unsigned)T), dim3(512),
-                       0, s, A, B, G, epi);
+    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKIND, Epi, 2, 2, 64, 4, kTileA16>), dim3((unsigned)T),
+                       dim3(512), 0, s, A, B, G, epi);
   else
     hipLaunchKernelGGL((gemm_kernel<DT, AK, BKIND, Epi>), dim3((unsigned)T), dim3(256), 0, s, A,
                        B, G, epi);
@@ -917,9 +923,10 @@ hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
                            int64_t V, float2 *partials, int64_t ld_part, const int *boff,
                            const unsigned *bent, float *zg, int32_t K, void *u, int64_t V_pad,
                            int64_t C_alloc, hipStream_t s) {
+  // vocabulary tiles cover V_pad (a multiple of the tile), so u is written for every row
   Operand A{W, d, (int)V, (int)d, 256};
   Operand B{h_c, d, (int)rows, (int)d, 256};
-  GemmGrid G{cdiv(V, kTile), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
+  GemmGrid G{(int)(V_pad / tile_rows(dtype)), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
   if (dtype == 1) {
     EpiFwdLse<1> e{partials, ld_part, (int)V, (int)rows, boff, bent, G.ntn, zg, (int)K, u,
                    C_alloc * 256, (int)V_pad};
@@ -931,14 +938,15 @@ hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
 }
 
 // Single-sweep backward: u = exp(z - m_g) from the forward epilogue (m_g the max of the
-// token's 128-row group g) becomes dz = sM * exp(z - lse) = sM * exp(m_g - lse) * u, in
-// place; bf16 also writes dzT (token-contiguous, zeros for tokens rows <= c < C_alloc).
-// A block takes 64 vocabulary rows (one group) x 64 tokens and transposes through LDS.
+// token's group g of gr = tile_rows / 2 vocabulary rows) becomes dz = sM * exp(z - lse) =
+// sM * exp(m_g - lse) * u, in place; bf16 also writes dzT (token-contiguous, zeros for
+// tokens rows <= c < C_alloc).  A block takes 64 vocabulary rows (inside one group, as
+// 64 divides gr) x 64 tokens and transposes through LDS.
 template <int DT>
 __global__ __launch_bounds__(256) void k_rescale_dz(void *dz, long long ts, unsigned short *dzt,
                                                     long long ldt, const float2 *part,
                                                     long long ld, const float *lse,
-                                                    const float *sM, int rows, int V) {
+                                                    const float *sM, int rows, int V, int gr) {
   __shared__ float f[64];
   __shared__ __attribute__((aligned(16))) unsigned short t[64][72];
   const int v0 = blockIdx.x * 64, c0 = blockIdx.y * 64, tid = threadIdx.x;
@@ -946,7 +954,7 @@ __global__ __launch_bounds__(256) void k_rescale_dz(void *dz, long long ts, unsi
     const int c = c0 + tid;
     float fc = 0.f;
     if (c < rows && v0 < V)
-      fc = sM[c] * fast_exp2((part[(long long)(v0 / kLseRows) * ld + c].x - lse[c]) * kLog2e);
+      fc = sM[c] * fast_exp2((part[(long long)(v0 / gr) * ld + c].x - lse[c]) * kLog2e);
     f[tid] = fc;
   }
   __syncthreads();
@@ -998,11 +1006,11 @@ hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, const float2 *parti
   if (dtype == 1)
     hipLaunchKernelGGL(k_rescale_dz<1>, grid, dim3(256), 0, s, dz, (long long)C_alloc * 256,
                        (unsigned short *)dzt, (long long)C_alloc, partials, (long long)C_alloc,
-                       lse, sM, (int)rows, (int)V);
+                       lse, sM, (int)rows, (int)V, tile_rows(1) / 2);
   else
     hipLaunchKernelGGL(k_rescale_dz<0>, grid, dim3(256), 0, s, dz, (long long)C_alloc * 256,
                        (unsigned short *)nullptr, 0LL, partials, (long long)C_alloc, lse, sM,
-                       (int)rows, (int)V);
+                       (int)rows, (int)V, tile_rows(0) / 2);
   return hipGetLastError();
 }
 
@@ -1011,7 +1019,7 @@ hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
                            int64_t V_pad, int64_t C_alloc, hipStream_t s) {
   Operand A{W, d, (int)V, (int)d, 256};
   Operand B{h_c, d, (int)rows, (int)d, 256};
-  GemmGrid G{cdiv(V, kTile), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
+  GemmGrid G{(int)(V_pad / tile_rows(dtype)), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
   if (dtype == 1) {
     EpiBwdDz<1> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows, (int)V_pad,
                   (unsigned short *)dzt, C_alloc};
@@ -1026,7 +1034,7 @@ hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, const void *
                           float *part, int64_t d_pad, int64_t C_alloc, hipStream_t s) {
   // D[j][c] = sum_v W[v][j] dz[c][v]; B = dz as KC ([c][v] in 256-column blocks).
   Operand B{dz, 256, (int)rows, (int)V_pad, C_alloc * 256};
-  GemmGrid G{cdiv(d, kTile), cdiv(rows, kTile), nsplit, (int)k_split, (int)V_pad, 0};
+  GemmGrid G{cdiv(d, tile_rows(dtype)), cdiv(rows, kTile), nsplit, (int)k_split, (int)V_pad, 0};
   EpiDhPart e{part, C_alloc * d_pad, d_pad, (int)rows};
   if (dtype == 1) {
     // A = W^T as KC: [j][v] in blocks of 256 v, zero-padded to V_pad, so both operands
@@ -1079,7 +1087,7 @@ hipError_t launch_dw_gemm(int dtype, const void *dz, const void *dzt, const void
                           const void *ht, int64_t rows, int64_t d, int64_t V, int64_t V_pad,
                           int64_t C_alloc, float *dW, int accumulate, hipStream_t s) {
   // D[v][j] = sum_c dz[c][v] h[c][j]
-  GemmGrid G{cdiv(V, kTile), cdiv(d, kTile), 1, (int)rows, (int)rows, 0};
+  GemmGrid G{cdiv(V, tile_rows(dtype)), cdiv(d, kTile), 1, (int)rows, (int)rows, 0};
   EpiDw e{dW, (int)d, (int)V, accumulate};
   if (dtype == 1) {
     // A = dzT ([v][c]), B = hT ([j][c]): both token-contiguous (KC)
@@ -1187,14 +1195,14 @@ hipError_t launch_validate(const int32_t *idx, const float *p, int64_t NK, int64
 
 // ---------------------------------------------------------------------------------
 // Buckets of teacher hits per output tile of the logits GEMMs (a counting sort).
-// Key of entry (row r, k) of a chunk: (idx >> 8) * ntn + (r >> 8).  A block takes 8 rows,
+// Key of entry (row r, k) of a chunk: (idx / tv) * ntn + (r >> 8).  A block takes 8 rows,
 // which share one token tile, and aggregates its keys in LDS before touching global
 // counters (the Zipf head puts about half of all hits in the first vocabulary tile).
 // With more than kBucketLdsBins vocabulary tiles the blocks count in global memory.
 // ---------------------------------------------------------------------------------
 constexpr int kBucketLdsBins = 8192;
 
-__global__ void k_bucket_count(const int32_t *idx, int rows, int K, int ntm, int ntn,
+__global__ void k_bucket_count(const int32_t *idx, int rows, int K, int tv, int ntm, int ntn,
                                int *counts) {
   extern __shared__ int hist[];
   const int t = threadIdx.x;
@@ -1207,13 +1215,13 @@ __global__ void k_bucket_count(const int32_t *idx, int rows, int K, int ntm, int
     for (int i = t; i < ntm; i += blockDim.x) hist[i] = 0;
     __syncthreads();
     for (int e = t; e < n; e += blockDim.x)
-      if (ip[e] >= 0) atomicAdd(&hist[ip[e] >> 8], 1);
+      if (ip[e] >= 0) atomicAdd(&hist[ip[e] / tv], 1);
     __syncthreads();
     for (int i = t; i < ntm; i += blockDim.x)
       if (hist[i]) atomicAdd(&counts[i * ntn + tn], hist[i]);
   } else {
     for (int e = t; e < n; e += blockDim.x)
-      if (ip[e] >= 0) atomicAdd(&counts[(ip[e] >> 8) * ntn + tn], 1);
+      if (ip[e] >= 0) atomicAdd(&counts[(ip[e] / tv) * ntn + tn], 1);
   }
 }
 
@@ -1244,7 +1252,7 @@ __global__ void k_bucket_scan(int *counts, int nkeys, int *offsets, int *cursor)
   if (t == 1023) offsets[nkeys] = part[1023];
 }
 
-__global__ void k_bucket_fill(const int32_t *idx, int rows, int K, int ntm, int ntn,
+__global__ void k_bucket_fill(const int32_t *idx, int rows, int K, int tv, int ntm, int ntn,
                               const int *offsets, int *cursor, unsigned *entries) {
   extern __shared__ int sh[];
   const int t = threadIdx.x;
@@ -1258,7 +1266,7 @@ __global__ void k_bucket_fill(const int32_t *idx, int rows, int K, int ntm, int 
     for (int i = t; i < ntm; i += blockDim.x) hist[i] = 0;
     __syncthreads();
     for (int e = t; e < n; e += blockDim.x)
-      if (ip[e] >= 0) atomicAdd(&hist[ip[e] >> 8], 1);
+      if (ip[e] >= 0) atomicAdd(&hist[ip[e] / tv], 1);
     __syncthreads();
     for (int i = t; i < ntm; i += blockDim.x)
       if (hist[i]) {
@@ -1270,27 +1278,28 @@ __global__ void k_bucket_fill(const int32_t *idx, int rows, int K, int ntm, int 
   for (int e = t; e < n; e += blockDim.x) {
     const int v = ip[e];
     if (v < 0) continue;  // outside this vocabulary shard
-    const int bin = v >> 8, q = e / K, r = r0 + q, k = e - q * K;
+    const int bin = v / tv, q = e / K, r = r0 + q, k = e - q * K;
     const int pos = lds ? base[bin] + atomicAdd(&hist[bin], 1)
                         : offsets[bin * ntn + tn] + atomicAdd(&cursor[bin * ntn + tn], 1);
-    entries[pos] = (unsigned)(r & 255) | ((unsigned)(v & 255) << 8) | ((unsigned)k << 16);
+    entries[pos] = (unsigned)(r & 255) | ((unsigned)(v - bin * tv) << 8) | ((unsigned)k << 17);
   }
 }
 
-hipError_t launch_buckets(const int32_t *idx_c, int64_t rows, int32_t K, int64_t V, int *counts,
-                          int *cursor, int *offsets, unsigned *entries, hipStream_t s) {
-  const int ntm = (int)((V + kTile - 1) / kTile), ntn = (int)((rows + kTile - 1) / kTile);
+hipError_t launch_buckets(const int32_t *idx_c, int64_t rows, int32_t K, int tv, int ntv,
+                          int *counts, int *cursor, int *offsets, unsigned *entries,
+                          hipStream_t s) {
+  const int ntm = ntv, ntn = (int)((rows + kTile - 1) / kTile);
   const int blocks = (int)((rows + 7) / 8);
   const bool lds = ntm <= kBucketLdsBins;
   hipLaunchKernelGGL(k_bucket_count, dim3(blocks), dim3(256), lds ? ntm * 4 : 0, s, idx_c,
-                     (int)rows, (int)K, ntm, ntn, counts);
+                     (int)rows, (int)K, tv, ntm, ntn, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, counts, ntm * ntn, offsets, cursor);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bucket_fill, dim3(blocks), dim3(256), lds ? 2 * ntm * 4 : 0, s, idx_c,
-                     (int)rows, (int)K, ntm, ntn, offsets, cursor, entries);
+                     (int)rows, (int)K, tv, ntm, ntn, offsets, cursor, entries);
   return hipGetLastError();
 }
 
