@@ -141,8 +141,10 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->off_bent = take((size_t)L->C_alloc * K * 4);
   L->off_wt = take(dtype == KD_BF16 ? (size_t)L->V_pad * d * 2 : 0);
   L->off_idxloc = take((size_t)L->C_alloc * K * 4);
-  L->off_dzt = take(dtype == KD_BF16 ? (size_t)L->V_pad * L->C_alloc * 2 : 0);
-  L->off_ht = take(dtype == KD_BF16 ? (size_t)d * L->C_alloc * 2 : 0);
+  L->dw_group = dtype == KD_BF16 && L->C_alloc < kDwGroupTokens
+                    ? (int)(kDwGroupTokens / L->C_alloc) : 1;
+  L->off_dzt = take(dtype == KD_BF16 ? (size_t)L->V_pad * L->dw_group * L->C_alloc * 2 : 0);
+  L->off_ht = take(dtype == KD_BF16 ? (size_t)d * L->dw_group * L->C_alloc * 2 : 0);
   L->total = off;
   return true;
 }
@@ -288,7 +290,7 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
   if (backward && dtype == KD_BF16)
     LAUNCH(kd::KC_TRANSPOSE, kd::launch_transpose_w(W, V, d, L.V_pad, WT, stream));
 
-  int chunk_i = 0;
+  int chunk_i = 0, dw_launches = 0;
   for (int64_t c0 = 0; c0 < N; c0 += L.C, ++chunk_i) {
     const int64_t rows = (N - c0) < L.C ? (N - c0) : L.C;
     const char *h_c = (const char *)h + c0 * d * es;
@@ -331,23 +333,35 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
                                                   srow, stream));
     }
     if (!backward) continue;
+    // This chunk's columns in the token-contiguous dW operands (dw_group chunks side by
+    // side; fp32 has none and multiplies each chunk's dz directly).
+    const int slot = chunk_i % L.dw_group;
+    const int64_t ldt = (int64_t)L.dw_group * L.C_alloc;
+    void *dzt_c = dzt ? (void *)((char *)dzt + (size_t)slot * L.C_alloc * 2) : nullptr;
+    void *ht_c = ht ? (void *)((char *)ht + (size_t)slot * L.C_alloc * 2) : nullptr;
     if (mode == M_FUSED)
-      LAUNCH(kd::KC_RESCALE, kd::launch_rescale_dz(dtype, dz, dzt, partials, lse_c, sM, rows, V,
-                                                   L.V_pad, L.C_alloc, stream));
+      LAUNCH(kd::KC_RESCALE, kd::launch_rescale_dz(dtype, dz, dzt_c, ldt, partials, lse_c, sM, rows,
+                                                   V, L.V_pad, L.C_alloc, stream));
     else
-      LAUNCH(kd::KC_BWD_GEMM, kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse_c, sM, dz, dzt,
-                                                  L.V_pad, L.C_alloc, stream));
-    LAUNCH(kd::KC_SCATTER,
-           kd::launch_scatter(dtype, dz, dzt, L.C_alloc, idx_k, p_c, srow, rows, K, stream));
+      LAUNCH(kd::KC_BWD_GEMM, kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse_c, sM, dz, dzt_c,
+                                                  ldt, L.V_pad, L.C_alloc, stream));
+    LAUNCH(kd::KC_SCATTER, kd::launch_scatter(dtype, dz, dzt_c, ldt, L.C_alloc, idx_k, p_c, srow,
+                                              rows, K, stream));
     LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, WT, rows, d, V, L.V_pad, L.nsplit,
                                               L.k_split, dhpart, L.d_pad, L.C_alloc, stream));
     LAUNCH(kd::KC_DH_REDUCE,
            kd::launch_dh_reduce(mode == M_SBWD ? (int)KD_F32 : dtype, dhpart, L.nsplit, L.C_alloc,
                                 L.d_pad, rows, d, (char *)dh + c0 * d * es_dh, stream));
-    if (ht)
-      LAUNCH(kd::KC_TRANSPOSE, kd::launch_transpose_h(h_c, rows, d, L.C_alloc, ht, stream));
-    LAUNCH(kd::KC_DW_GEMM, kd::launch_dw_gemm(dtype, dz, dzt, h_c, ht, rows, d, V, L.V_pad,
-                                              L.C_alloc, dW, chunk_i > 0, stream));
+    if (ht_c)
+      LAUNCH(kd::KC_TRANSPOSE,
+             kd::launch_transpose_h(h_c, rows, d, L.C_alloc, ht_c, ldt, stream));
+    if (slot == L.dw_group - 1 || c0 + rows >= N) {
+      // every earlier chunk of the group is whole: its columns past C are zero
+      const int64_t k = (int64_t)slot * L.C_alloc + rows;
+      LAUNCH(kd::KC_DW_GEMM, kd::launch_dw_gemm(dtype, dz, dzt, h_c, ht, ldt, k, d, V, L.V_pad,
+                                                L.C_alloc, dW, dw_launches > 0, stream));
+      ++dw_launches;
+    }
   }
   if (fwd && !shard && count > 0)
     LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));

@@ -998,14 +998,14 @@ __global__ __launch_bounds__(256) void k_rescale_dz(void *dz, long long ts, unsi
   }
 }
 
-hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, const float2 *partials,
+hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, int64_t ldt, const float2 *partials,
                              const float *lse, const float *sM, int64_t rows, int64_t V,
                              int64_t V_pad, int64_t C_alloc, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)(V_pad / 64), (unsigned)(C_alloc / 64));
   if (dtype == 1)
     hipLaunchKernelGGL(k_rescale_dz<1>, grid, dim3(256), 0, s, dz, (long long)C_alloc * 256,
-                       (unsigned short *)dzt, (long long)C_alloc, partials, (long long)C_alloc,
+                       (unsigned short *)dzt, (long long)ldt, partials, (long long)C_alloc,
                        lse, sM, (int)rows, (int)V, tile_rows(1) / 2);
   else
     hipLaunchKernelGGL(k_rescale_dz<0>, grid, dim3(256), 0, s, dz, (long long)C_alloc * 256,
@@ -1016,13 +1016,13 @@ hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, const float2 *parti
 
 hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
                            int64_t V, const float *lse, const float *sM, void *dz, void *dzt,
-                           int64_t V_pad, int64_t C_alloc, hipStream_t s) {
+                           int64_t ldt, int64_t V_pad, int64_t C_alloc, hipStream_t s) {
   Operand A{W, d, (int)V, (int)d, 256};
   Operand B{h_c, d, (int)rows, (int)d, 256};
   GemmGrid G{(int)(V_pad / tile_rows(dtype)), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
   if (dtype == 1) {
     EpiBwdDz<1> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows, (int)V_pad,
-                  (unsigned short *)dzt, C_alloc};
+                  (unsigned short *)dzt, ldt};
     return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
   }
   EpiBwdDz<0> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows, (int)V_pad, nullptr, 0};
@@ -1084,26 +1084,28 @@ hipError_t launch_transpose_w(const void *W, int64_t V, int64_t d, int64_t V_pad
 }
 
 hipError_t launch_dw_gemm(int dtype, const void *dz, const void *dzt, const void *h_c,
-                          const void *ht, int64_t rows, int64_t d, int64_t V, int64_t V_pad,
-                          int64_t C_alloc, float *dW, int accumulate, hipStream_t s) {
-  // D[v][j] = sum_c dz[c][v] h[c][j]
-  GemmGrid G{cdiv(V, tile_rows(dtype)), cdiv(d, kTile), 1, (int)rows, (int)rows, 0};
+                          const void *ht, int64_t ldt, int64_t k, int64_t d, int64_t V,
+                          int64_t V_pad, int64_t C_alloc, float *dW, int accumulate,
+                          hipStream_t s) {
+  // D[v][j] = sum_c dz[c][v] h[c][j] over k tokens
+  GemmGrid G{cdiv(V, tile_rows(dtype)), cdiv(d, kTile), 1, (int)k, (int)k, 0};
   EpiDw e{dW, (int)d, (int)V, accumulate};
   if (dtype == 1) {
     // A = dzT ([v][c]), B = hT ([j][c]): both token-contiguous (KC)
-    Operand A{dzt, C_alloc, (int)V, (int)rows, 256};
-    Operand B{ht, C_alloc, (int)d, (int)rows, 256};
+    Operand A{dzt, ldt, (int)V, (int)k, 256};
+    Operand B{ht, ldt, (int)d, (int)k, 256};
     return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
   }
   // A = dz as MC ([c][v] in 256-column blocks), B = h as MC ([c][j])
-  Operand A{dz, 256, (int)V_pad, (int)rows, C_alloc * 256};
-  Operand B{h_c, d, (int)d, (int)rows, 256};
+  Operand A{dz, 256, (int)V_pad, (int)k, C_alloc * 256};
+  Operand B{h_c, d, (int)d, (int)k, 256};
   return run_gemm<0, OP_MC, OP_MC>(A, B, G, e, s);
 }
 
-// h chunk [rows][d] -> hT [d][ldt] (bf16), through a 64 x 64 LDS tile.
-__global__ __launch_bounds__(256) void k_transpose_h(const unsigned short *h, int rows, int d,
-                                                     long long ldt, unsigned short *ht) {
+// h chunk [rows][d] -> hT [d][ldt] (bf16), columns c < ncols (zero for c >= rows), through
+// a 64 x 64 LDS tile.
+__global__ __launch_bounds__(256) void k_transpose_h(const unsigned short *h, int rows, int ncols,
+                                                     int d, long long ldt, unsigned short *ht) {
   __shared__ __attribute__((aligned(16))) unsigned short t[64][72];
   const int c0 = blockIdx.x * 64, j0 = blockIdx.y * 64, tid = threadIdx.x;
 #pragma unroll
@@ -1119,21 +1121,21 @@ __global__ __launch_bounds__(256) void k_transpose_h(const unsigned short *h, in
   for (int q = tid; q < 512; q += 256) {
     const int jr = q >> 3, c8 = (q & 7) * 8;
     const int j = j0 + jr, c = c0 + c8;
-    if (j >= d || c >= rows) continue;
+    if (j >= d || c >= ncols) continue;
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       o[e] = (unsigned)t[c8 + 2 * e][jr] | ((unsigned)t[c8 + 2 * e + 1][jr] << 16);
-    *(u32x4 *)(ht + (long long)j * ldt + c) = o;  // ldt % 8 == 0: columns up to c+7 < ldt
+    *(u32x4 *)(ht + (long long)j * ldt + c) = o;  // ncols % 8 == 0
   }
 }
 
-hipError_t launch_transpose_h(const void *h_c, int64_t rows, int64_t d, int64_t C_alloc, void *ht,
-                              hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((d + 63) / 64));
+hipError_t launch_transpose_h(const void *h_c, int64_t rows, int64_t d, int64_t C_alloc,
+                              void *ht, int64_t ldt, hipStream_t s) {
+  if (C_alloc <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(C_alloc / 64), (unsigned)((d + 63) / 64));
   hipLaunchKernelGGL(k_transpose_h, grid, dim3(256), 0, s, (const unsigned short *)h_c, (int)rows,
-                     (int)d, (long long)C_alloc, (unsigned short *)ht);
+                     (int)C_alloc, (int)d, (long long)ldt, (unsigned short *)ht);
   return hipGetLastError();
 }
 
@@ -1502,13 +1504,13 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigne
   }
 }
 
-hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t C_alloc, const int32_t *idx_c,
-                          const float *p_c, const float *srow, int64_t rows, int32_t K,
-                          hipStream_t s) {
+hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t ldt, int64_t C_alloc,
+                          const int32_t *idx_c, const float *p_c, const float *srow, int64_t rows,
+                          int32_t K, hipStream_t s) {
   const int blocks = (int)((rows + 3) / 4);
   if (dtype == 1)
     hipLaunchKernelGGL(k_scatter<1>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256,
-                       (unsigned short *)dzt, (long long)C_alloc, idx_c, p_c, srow, (int)rows,
+                       (unsigned short *)dzt, (long long)ldt, idx_c, p_c, srow, (int)rows,
                        (int)K);
   else
     hipLaunchKernelGGL(k_scatter<0>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256,
