@@ -15,6 +15,7 @@
 #include "kd_internal.h"
 
 #include <cstdint>
+#include <type_traits>
 
 namespace kd {
 
@@ -23,6 +24,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -941,16 +943,35 @@ hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
 // token's group g of gr = tile_rows / 2 vocabulary rows) becomes dz = sM * exp(z - lse) =
 // sM * exp(m_g - lse) * u, in place; bf16 also writes dzT (token-contiguous, zeros for
 // tokens rows <= c < C_alloc).  A block takes 64 vocabulary rows (inside one group, as
-// 64 divides gr) x 64 tokens and transposes through LDS.
-template <int DT>
+// 64 divides gr) x TC tokens and transposes through LDS.  Each thread first issues all
+// its loads of u (NQ chunks of 8 elements), then the factors are formed.
+template <int DT, int TC>
 __global__ __launch_bounds__(256) void k_rescale_dz(void *dz, long long ts, unsigned short *dzt,
                                                     long long ldt, const float2 *part,
                                                     long long ld, const float *lse,
                                                     const float *sM, int rows, int V, int gr) {
-  __shared__ float f[64];
-  __shared__ __attribute__((aligned(16))) unsigned short t[64][72];
-  const int v0 = blockIdx.x * 64, c0 = blockIdx.y * 64, tid = threadIdx.x;
-  if (tid < 64) {
+  constexpr int NQ = TC * 8 / 256;
+  __shared__ float f[TC];
+  // [TC tokens][64 rows], 16-B chunks of a token's row XOR-swizzled by token / 8 so that
+  // the column reads of the transpose hit at most two tokens per bank
+  __shared__ __attribute__((aligned(16))) unsigned short t[DT == 1 ? TC * 64 : 8];
+  auto tix = [](int c, int v) { return c * 64 + ((((v >> 3) ^ (c >> 3)) & 7) << 3) + (v & 7); };
+  const int v0 = blockIdx.x * 64, c0 = blockIdx.y * TC, tid = threadIdx.x;
+  using Chunk = typename std::conditional<DT == 1, u32x4, f32x8>::type;
+  Chunk in[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int q = tid + j * 256, r = q >> 3, v = v0 + (q & 7) * 8, c = c0 + r;
+    in[j] = Chunk{};
+    if (c < rows) {
+      const long long o = (long long)(v >> 8) * ts + c * 256 + (v & 255);
+      if constexpr (DT == 1)
+        in[j] = *(const u32x4 *)((const unsigned short *)dz + o);
+      else
+        in[j] = *(const f32x8 *)((const float *)dz + o);
+    }
+  }
+  if (tid < TC) {
     const int c = c0 + tid;
     float fc = 0.f;
     if (c < rows && v0 < V)
@@ -959,42 +980,39 @@ __global__ __launch_bounds__(256) void k_rescale_dz(void *dz, long long ts, unsi
   }
   __syncthreads();
 #pragma unroll
-  for (int q = tid; q < 512; q += 256) {
-    const int r = q >> 3, v8 = (q & 7) * 8;
-    const int c = c0 + r, v = v0 + v8;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (c < rows) {
-      const float a = f[r];
-      const long long o = (long long)(v >> 8) * ts + c * 256 + (v & 255);
-      if (DT == 1) {
-        u32x4 *pp = (u32x4 *)((unsigned short *)dz + o);
-        const u32x4 in = *pp;
+  for (int j = 0; j < NQ; ++j) {
+    const int q = tid + j * 256, r = q >> 3, v8 = (q & 7) * 8, v = v0 + v8, c = c0 + r;
+    const float a = f[r];
+    const long long o = (long long)(v >> 8) * ts + c * 256 + (v & 255);
+    if constexpr (DT == 1) {
+      u32x4 val;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          val[e] = pack_bf16x2(a * bf16_to_f32((unsigned short)(in[e] & 0xFFFFu)),
-                               a * bf16_to_f32((unsigned short)(in[e] >> 16)));
-        *pp = val;
-      } else {
-        f32x4 *pp = (f32x4 *)((float *)dz + o);
+      for (int e = 0; e < 4; ++e)
+        val[e] = pack_bf16x2(a * bf16_to_f32((unsigned short)(in[j][e] & 0xFFFFu)),
+                             a * bf16_to_f32((unsigned short)(in[j][e] >> 16)));
+      if (c < rows) *(u32x4 *)((unsigned short *)dz + o) = val;
+      *(u32x4 *)&t[tix(r, v8)] = val;  // zero for c >= rows (a = 0, u = 0)
+    } else {
+      if (c < rows) {
+        f32x8 x = in[j];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f32x4 x = pp[h];
-          pp[h] = f32x4{a * x[0], a * x[1], a * x[2], a * x[3]};
-        }
+        for (int e = 0; e < 8; ++e) x[e] *= a;
+        *(f32x8 *)((float *)dz + o) = x;
       }
     }
-    if (DT == 1) *(u32x4 *)&t[r][v8] = val;
   }
-  if (DT == 0) return;
-  __syncthreads();
+  if constexpr (DT == 1) {
+    __syncthreads();
+    // dzT: 64 rows of TC tokens, 16 B per lane
 #pragma unroll
-  for (int q = tid; q < 512; q += 256) {
-    const int vr = q >> 3, c8 = (q & 7) * 8;
-    u32x4 o;
+    for (int j = 0; j < NQ; ++j) {
+      const int q = tid + j * 256, vr = q / (TC / 8), c8 = (q % (TC / 8)) * 8;
+      u32x4 o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = (unsigned)t[c8 + 2 * e][vr] | ((unsigned)t[c8 + 2 * e + 1][vr] << 16);
-    *(u32x4 *)(dzt + (long long)(v0 + vr) * ldt + c0 + c8) = o;
+      for (int e = 0; e < 4; ++e)
+        o[e] = (unsigned)t[tix(c8 + 2 * e, vr)] | ((unsigned)t[tix(c8 + 2 * e + 1, vr)] << 16);
+      *(u32x4 *)(dzt + (long long)(v0 + vr) * ldt + c0 + c8) = o;
+    }
   }
 }
 
@@ -1002,15 +1020,15 @@ hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, int64_t ldt, const 
                              const float *lse, const float *sM, int64_t rows, int64_t V,
                              int64_t V_pad, int64_t C_alloc, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const dim3 grid((unsigned)(V_pad / 64), (unsigned)(C_alloc / 64));
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_rescale_dz<1>, grid, dim3(256), 0, s, dz, (long long)C_alloc * 256,
-                       (unsigned short *)dzt, (long long)ldt, partials, (long long)C_alloc,
-                       lse, sM, (int)rows, (int)V, tile_rows(1) / 2);
+  if (dtype == 1)  // C_alloc is a multiple of 256
+    hipLaunchKernelGGL((k_rescale_dz<1, 128>), dim3((unsigned)(V_pad / 64), (unsigned)(C_alloc / 128)),
+                       dim3(256), 0, s, dz, (long long)C_alloc * 256, (unsigned short *)dzt,
+                       (long long)ldt, partials, (long long)C_alloc, lse, sM, (int)rows, (int)V,
+                       tile_rows(1) / 2);
   else
-    hipLaunchKernelGGL(k_rescale_dz<0>, grid, dim3(256), 0, s, dz, (long long)C_alloc * 256,
-                       (unsigned short *)nullptr, 0LL, partials, (long long)C_alloc, lse, sM,
-                       (int)rows, (int)V, tile_rows(0) / 2);
+    hipLaunchKernelGGL((k_rescale_dz<0, 64>), dim3((unsigned)(V_pad / 64), (unsigned)(C_alloc / 64)),
+                       dim3(256), 0, s, dz, (long long)C_alloc * 256, (unsigned short *)nullptr, 0LL,
+                       partials, (long long)C_alloc, lse, sM, (int)rows, (int)V, tile_rows(0) / 2);
   return hipGetLastError();
 }
 
