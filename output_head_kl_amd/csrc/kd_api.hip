@@ -110,7 +110,7 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   // Split the vocabulary of the dh GEMM so that two (bf16) or three (fp32) workgroups
   // per CU run.
   const int64_t tiles = ((d + L->tv - 1) / L->tv) * (L->C_alloc / kTile);
-  const int64_t target = dtype == KD_BF16 ? 512 : 768;
+  const int64_t target = dtype == KD_BF16 ? 256 : 768;
   int64_t ns = (target + tiles - 1) / tiles;
   const int64_t max_by_k = L->V_pad / kTile;  // at least one dz column block per split
   if (ns > max_by_k) ns = max_by_k;
