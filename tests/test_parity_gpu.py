@@ -56,6 +56,20 @@ def test_ragged_shapes_in_full(torch_cuda, dtype):
     _check_full(inp, run(inp, torch_cuda))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_wide_logit_range(torch_cuda, dtype):
+    """Logits with a standard deviation near 60: for most 192-row vocabulary groups of a
+    token exp(group max - lse) underflows to zero, so the fused call's kept exponentials
+    are scaled by zero there and teacher entries in those groups leave the sparse term
+    alone in dz."""
+    inp = synth.make(1, seed=21, N=300, d=128, V=5000, K=12, chunk=128, dtype=dtype)
+    if dtype == "bf16":
+        inp.W = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp.W) * 30.0)
+    else:
+        inp.W = (inp.W * 30.0).astype(np.float32)
+    _check_full(inp, run(inp, torch_cuda))
+
+
 def test_tiny_chunks_and_single_token(torch_cuda):
     inp = synth.make(0, seed=5, N=37, d=8, V=300, K=3, chunk=1, dtype="bf16")
     _check_full(inp, run(inp, torch_cuda))
