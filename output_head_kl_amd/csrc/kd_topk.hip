@@ -5,12 +5,15 @@
 // "Select top 100"); the loss reads them as probabilities (aimodeling.com article,
 // "First cut").
 //
-// One workgroup (4 waves) per row reads the row from HBM exactly once:
+// One workgroup (2 waves) per row reads the row from HBM exactly once.  Small
+// workgroups with a small candidate buffer (12 KB of LDS) keep about 10 rows in flight
+// per CU, which is what keeps HBM busy; their barriers are cheap.
 //  * streaming pass: 16-byte loads per lane; an online (max, sum exp) per lane for the
 //    logsumexp; every element whose order-preserving key reaches the running
 //    threshold is appended to an LDS candidate buffer (one LDS atomic per wave per
 //    chunk);
-//  * every GROUP chunks, if the buffer could overflow on the next group, a radix select
+//  * after every GROUP chunks (one chunk of 1024 bf16 or two of 512 fp32), if the
+//    buffer could overflow on the next group, a radix select
 //    over the buffer keeps exactly the K best candidates and raises the threshold;
 //  * the selection key is unique: (value key << 32) | ~index, so equal logits are
 //    ordered by increasing token index and the result does not depend on timing;
@@ -26,7 +29,7 @@ namespace {
 
 constexpr float kTkLog2e = 1.4426950408889634f;
 constexpr float kTkLn2 = 0.6931471805599453f;
-constexpr int kTkThreads = 256;
+constexpr int kTkThreads = 128;
 
 // Workgroup barrier that orders LDS accesses only: every exchange between threads in
 // this kernel goes through LDS, and a full __syncthreads would also wait for the
@@ -83,12 +86,17 @@ __device__ __forceinline__ uint64_t comp_key(uint32_t vk, uint32_t idx) {
 template <int TB>
 __device__ void radix_select(const uint64_t *s_ck, int n, int need, uint32_t *s_hist,
                              uint64_t *s_res, int t) {
+  constexpr int NB = 256 / kTkThreads;  // bins per thread: t owns bins NB*t .. NB*t+NB-1
+  constexpr int NWV = kTkThreads / 64;
+  static_assert(NB * kTkThreads == 256 && NWV >= 1 && NWV <= 4, "block shape");
   uint64_t P = 0;
   int D = 0;
   __shared__ int s_bin, s_above, s_inbin;
+  __shared__ uint32_t s_wtot[4];
   for (int level = 0; level < TB / 8; ++level) {
     const int shift = TB - 8 * (level + 1);
-    s_hist[t] = 0u;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) s_hist[NB * t + j] = 0u;
     lds_sync();
     // entries whose digits above this level equal the prefix (at the first level of a
     // 64-bit key every entry matches: a shift by 64 would be undefined)
@@ -98,25 +106,36 @@ __device__ void radix_select(const uint64_t *s_ck, int n, int need, uint32_t *s_
       if (all || (c >> (shift + 8)) == P) atomicAdd(&s_hist[(c >> shift) & 255u], 1u);
     }
     lds_sync();
-    // suffix sums over the 256 bins: wave w holds bins 64w..64w+63
+    // suffix sums over the 256 bins, from the top: this thread's bins, then the threads
+    // above it (lanes above in the wave, then the waves above)
     const int lane = t & 63, w = t >> 6;
-    const uint32_t h = s_hist[t];
-    uint32_t sfx = h;  // inclusive suffix within the wave
+    uint32_t h[NB], own = 0;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      h[j] = s_hist[NB * t + j];
+      own += h[j];
+    }
+    uint32_t sfx = own;  // inclusive suffix of the thread totals within the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t y = __shfl_down(sfx, o, 64);
       if (lane + o < 64) sfx += y;
     }
-    __shared__ uint32_t s_wtot[4];
-    if (lane == 0) s_wtot[w] = sfx;
-    lds_sync();
-    uint32_t later = 0;
-    for (int w2 = w + 1; w2 < 4; ++w2) later += s_wtot[w2];
-    const uint32_t S = sfx + later;  // entries of this prefix with digit >= t
-    if (S >= (uint32_t)need && S - h < (uint32_t)need) {
-      s_bin = t;
-      s_above = (int)(S - h);
-      s_inbin = (int)h;
+    if (NWV > 1) {
+      if (lane == 0) s_wtot[w] = sfx;
+      lds_sync();
+    }
+    uint32_t later = sfx - own;  // threads above this one
+    for (int w2 = w + 1; w2 < NWV; ++w2) later += s_wtot[w2];
+    uint32_t S = later;  // entries of this prefix with digit >= the bin, accumulated down
+#pragma unroll
+    for (int j = NB - 1; j >= 0; --j) {
+      S += h[j];
+      if (S >= (uint32_t)need && S - h[j] < (uint32_t)need) {
+        s_bin = NB * t + j;
+        s_above = (int)(S - h[j]);
+        s_inbin = (int)h[j];
+      }
     }
     lds_sync();
     const int bin = s_bin, above = s_above, inbin = s_inbin;
@@ -168,7 +187,7 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
   using T = TkT<DT>;
   constexpr int EPL = VEC ? T::EPL : 1;
   constexpr int CHUNK = kTkThreads * EPL;
-  constexpr int GROUP = DT == 1 ? 2 : 4;                 // chunks between checkpoints
+  constexpr int GROUP = DT == 1 ? 1 : 2;                 // chunks between checkpoints
   constexpr int CAP = kTopkMaxK + GROUP * CHUNK;         // never overflows (see below)
   constexpr int TB = T::VB + 32;
   __shared__ uint64_t s_ck[CAP];
@@ -265,11 +284,12 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
       for (int j = 0; j < EPL; ++j) part += __builtin_amdgcn_exp2f((x[j] - m) * kTkLog2e);
       s += (double)part;
     }
-    // candidates (rare once the threshold has risen): skipped when no lane has one
-    int mycnt = 0;
+    // candidates (rare once the threshold has risen): skipped when no lane of the wave
+    // has one, which the lane maximum alone tells (a NaN is never a candidate)
+    if (__ballot(in && lm >= tf)) {
+      int mycnt = 0;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) mycnt += (in && x[j] >= tf) ? 1 : 0;
-    if (__ballot(mycnt > 0)) {
+      for (int j = 0; j < EPL; ++j) mycnt += (in && x[j] >= tf) ? 1 : 0;
       int incl = mycnt;  // inclusive prefix over the wave
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
