@@ -379,6 +379,10 @@ struct EpiFwdLse {
     __builtin_amdgcn_sched_barrier(0);
     // (max, sum exp) per wave row and token, and u
     const int vl = m0 + (lane >> 5) * 4;
+    if constexpr (DT == 1 && NRB % 3 == 0) {
+      staged_u(acc, m0, n0, lane, smem);
+      return;
+    }
     if (m0 < V) {
       const bool full = m0 + WR <= V;
 #pragma unroll
@@ -442,6 +446,84 @@ struct EpiFwdLse {
                   f32x4{0.f, 0.f, 0.f, 0.f};
           }
       }
+    }
+  }
+
+  // bf16, 192-row waves: as above, but u (when wanted) goes out through LDS so that the
+  // stores are whole 16-byte pieces of a token's vocabulary run (192 contiguous bytes
+  // per token and pass) instead of 8-byte pieces for 32 tokens at once.  Each wave
+  // stages its own 96 rows x 32*NCB tokens per pass in a private slice of LDS (13 KB);
+  // the workgroup barrier first lets every wave finish with the gather's staging buffer.
+  template <int NRB, int NCB>
+  __device__ __forceinline__ void staged_u(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
+                                           char *smem) const {
+    constexpr int WR = 32 * NRB, RP = 3, NP = NRB / RP;  // 32-row blocks per pass, passes
+    constexpr int TOK = 32 * NCB, PITCH = 104;            // tokens per wave, bf16 per row
+    constexpr int QPR = RP * 32 / 8;                      // 16-byte pieces per token row
+    const bool keep = u != nullptr;                       // the same for the workgroup
+    if (keep) __syncthreads();
+    LDS_AS unsigned short *stg =
+        (LDS_AS unsigned short *)smem + (threadIdx.x >> 6) * TOK * PITCH;
+    const int vl = m0 + (lane >> 5) * 4;
+    const bool live = m0 < V;                 // the wave has rows below V
+    const bool full = m0 + WR <= V;
+    float mx[NCB], sum[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
+          if (full || v < V) m = fmaxf(m, acc[rb][cb][i]);
+        }
+      mx[cb] = halves_max(m);
+      sum[cb] = 0.f;
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const float mx2 = mx[cb] * kLog2e;
+        const int cl = cb * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          const int rb = p * RP + r;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int v0 = vl + rb * 32 + g * 8;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[e] = live && (full || v0 + e < V)
+                         ? fast_exp2(fmaf(acc[rb][cb][g * 4 + e], kLog2e, -mx2))
+                         : 0.f;
+              sum[cb] += x[e];
+            }
+            if (keep) {
+              const u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+              *(LDS_AS u32x2 *)(stg + cl * PITCH + r * 32 + g * 8 + (lane >> 5) * 4) = pk;
+            }
+          }
+        }
+      }
+      if (!keep) continue;
+#pragma unroll
+      for (int it = 0; it < TOK * QPR / 64; ++it) {
+        const int q = it * 64 + lane, cl = q / QPR, pc = q - cl * QPR;
+        const int c = n0 + cl, v = m0 + p * RP * 32 + pc * 8;
+        const u32x4 val = *(const LDS_AS u32x4 *)(stg + cl * PITCH + pc * 8);
+        if (c < rows)
+          *(u32x4 *)((unsigned short *)u + (long long)(v >> 8) * ts + c * 256 + (v & 255)) = val;
+      }
+    }
+    if (!live) return;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const float sm = halves_sum(sum[cb]);
+      const int c = n0 + cb * 32 + (lane & 31);
+      if (lane < 32 && c < rows) part[(long long)(m0 / WR) * ld + c] = make_float2(mx[cb], sm);
     }
   }
 };
