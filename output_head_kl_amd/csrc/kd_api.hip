@@ -336,16 +336,17 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
     // This chunk's columns in the token-contiguous dW operands (dw_group chunks side by
     // side; fp32 has none and multiplies each chunk's dz directly).
     const int slot = chunk_i % L.dw_group;
-    const int64_t ldt = (int64_t)L.dw_group * L.C_alloc;
-    void *dzt_c = dzt ? (void *)((char *)dzt + (size_t)slot * L.C_alloc * 2) : nullptr;
-    void *ht_c = ht ? (void *)((char *)ht + (size_t)slot * L.C_alloc * 2) : nullptr;
+    // (token-blocked: the slot starts at token block slot * C_alloc / 256)
+    const int64_t tst_dz = L.V_pad * 256, tst_h = d * 256;
+    void *dzt_c = dzt ? (void *)((char *)dzt + (size_t)slot * L.C_alloc * L.V_pad * 2) : nullptr;
+    void *ht_c = ht ? (void *)((char *)ht + (size_t)slot * L.C_alloc * d * 2) : nullptr;
     if (mode == M_FUSED)
-      LAUNCH(kd::KC_RESCALE, kd::launch_rescale_dz(dtype, dz, dzt_c, ldt, partials, lse_c, sM, rows,
+      LAUNCH(kd::KC_RESCALE, kd::launch_rescale_dz(dtype, dz, dzt_c, tst_dz, partials, lse_c, sM, rows,
                                                    V, L.V_pad, L.C_alloc, stream));
     else
       LAUNCH(kd::KC_BWD_GEMM, kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse_c, sM, dz, dzt_c,
-                                                  ldt, L.V_pad, L.C_alloc, stream));
-    LAUNCH(kd::KC_SCATTER, kd::launch_scatter(dtype, dz, dzt_c, ldt, L.C_alloc, idx_k, p_c, srow,
+                                                  tst_dz, L.V_pad, L.C_alloc, stream));
+    LAUNCH(kd::KC_SCATTER, kd::launch_scatter(dtype, dz, dzt_c, tst_dz, L.C_alloc, idx_k, p_c, srow,
                                               rows, K, stream));
     LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, WT, rows, d, V, L.V_pad, L.nsplit,
                                               L.k_split, dhpart, L.d_pad, L.C_alloc, stream));
@@ -354,11 +355,11 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
                                 L.d_pad, rows, d, (char *)dh + c0 * d * es_dh, stream));
     if (ht_c)
       LAUNCH(kd::KC_TRANSPOSE,
-             kd::launch_transpose_h(h_c, rows, d, L.C_alloc, ht_c, ldt, stream));
+             kd::launch_transpose_h(h_c, rows, d, L.C_alloc, ht_c, tst_h, stream));
     if (slot == L.dw_group - 1 || c0 + rows >= N) {
       // every earlier chunk of the group is whole: its columns past C are zero
       const int64_t k = (int64_t)slot * L.C_alloc + rows;
-      LAUNCH(kd::KC_DW_GEMM, kd::launch_dw_gemm(dtype, dz, dzt, h_c, ht, ldt, k, d, V, L.V_pad,
+      LAUNCH(kd::KC_DW_GEMM, kd::launch_dw_gemm(dtype, dz, dzt, h_c, ht, k, d, V, L.V_pad,
                                                 L.C_alloc, dW, dw_launches > 0, stream));
       ++dw_launches;
     }

@@ -18,7 +18,7 @@ constexpr int kTileA16 = 384;
 inline int tile_rows(int dtype) { return dtype == 1 ? kTileA16 : kTile; }
 // Tokens per dW GEMM launch (bf16): each launch adds its product into the fp32 dW, a
 // read and a write of all of dW, so chunks are grouped up to this many tokens.
-constexpr int kDwGroupTokens = 4096;
+constexpr int kDwGroupTokens = 8192;
 
 // Kernel classes for timing (kd_profile_*).
 enum KClass {
@@ -78,9 +78,13 @@ hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
                            int64_t d, int64_t V, float2 *partials, int64_t ld_part,
                            const int *boff, const unsigned *bent, float *zg, int32_t K,
                            void *u, int64_t V_pad, int64_t C_alloc, hipStream_t s);
-// dz = sM * exp(m_g - lse) * u in place (and dzT, pitch ldt, for bf16), from the
-// forward's partials.
-hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, int64_t ldt, const float2 *partials,
+// Token-blocked layout of the dW GEMM's operands (bf16): element (r, c) of a matrix with
+// R rows over the tokens of a dW group at X[(c / 256) * tst + r * 256 + c % 256], with
+// tst = R * 256 (R = V_pad for dzT, d for hT).  Pointers passed per chunk point at the
+// chunk's first token block.
+//
+// dz = sM * exp(m_g - lse) * u in place (and dzT for bf16), from the forward's partials.
+hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, int64_t tst, const float2 *partials,
                              const float *lse, const float *sM, int64_t rows, int64_t V,
                              int64_t V_pad, int64_t C_alloc, hipStream_t s);
 hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part,
@@ -96,17 +100,18 @@ hipError_t launch_accum_loss(const double *rowterm, int64_t rows, double *acc, h
 hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s);
 // dz is stored as blocks of 256 vocabulary columns: element (c, v) at
 // dz[(v / 256) * C_alloc * 256 + c * 256 + v % 256].
-// bf16 also writes dzT, the same values token-contiguous: element (c, v) at
-// dzT[v * ldt + c] for v < V_pad, c < C_alloc (zero for c >= rows).
+// bf16 also writes dzT, the same values in the token-blocked layout (tst = V_pad * 256)
+// for v < V_pad, c < C_alloc (zero for c >= rows).
 hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
                            int64_t V, const float *lse, const float *sM, void *dz, void *dzt,
-                           int64_t ldt, int64_t V_pad, int64_t C_alloc, hipStream_t s);
-hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t ldt, int64_t C_alloc,
+                           int64_t tst, int64_t V_pad, int64_t C_alloc, hipStream_t s);
+hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t tst, int64_t C_alloc,
                           const int32_t *idx_c, const float *p_c, const float *srow, int64_t rows,
                           int32_t K, hipStream_t s);
-// h chunk [rows][d] bf16 -> hT [d][ldt], columns c < C_alloc (zero for c >= rows).
+// h chunk [rows][d] bf16 -> hT in the token-blocked layout (tst = d * 256), columns
+// c < C_alloc (zero for c >= rows).
 hipError_t launch_transpose_h(const void *h_c, int64_t rows, int64_t d, int64_t C_alloc,
-                              void *ht, int64_t ldt, hipStream_t s);
+                              void *ht, int64_t tst, hipStream_t s);
 // W^T in blocks of 256 vocabulary entries (bf16 only): element (v, j) of W at
 // WT[(v / 256) * d * 256 + j * 256 + v % 256], zero for V <= v < V_pad.
 hipError_t launch_transpose_w(const void *W, int64_t V, int64_t d, int64_t V_pad, void *WT,
@@ -117,10 +122,10 @@ hipError_t launch_dh_gemm(int dtype, const void *dz, const void *W, const void *
                           float *part, int64_t d_pad, int64_t C_alloc, hipStream_t s);
 hipError_t launch_dh_reduce(int dtype, const float *part, int nsplit, int64_t C_alloc,
                             int64_t d_pad, int64_t rows, int64_t d, void *dh, hipStream_t s);
-// dW (+)= dz^T h over k tokens: bf16 reads dzT and hT (both token-contiguous, pitch
-// ldt, k <= ldt), fp32 reads one chunk's dz (k = rows) and h.
+// dW (+)= dz^T h over k tokens: bf16 reads dzT and hT (token-blocked, k tokens of the
+// group), fp32 reads one chunk's dz (k = rows) and h.
 hipError_t launch_dw_gemm(int dtype, const void *dz, const void *dzt, const void *h_c,
-                          const void *ht, int64_t ldt, int64_t k, int64_t d, int64_t V,
+                          const void *ht, int64_t k, int64_t d, int64_t V,
                           int64_t V_pad, int64_t C_alloc, float *dW, int accumulate,
                           hipStream_t s);
 

@@ -39,14 +39,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
   return __uint_as_float(((unsigned int)b) << 16);
 }
-// Round to nearest, ties to even (inputs are finite).
-__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
-  unsigned int u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
-}
+// Round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32 converts two floats in one
+// instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
-  return (unsigned int)f32_to_bf16(lo) | ((unsigned int)f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  return (unsigned short)(pack_bf16x2(f, 0.f) & 0xFFFFu);
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -321,7 +322,7 @@ void gemm_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
 //    tile, entries packed c_local | v_local << 8 | k << 17) read z from the tile, staged
 //    through LDS in slices of 64 vocabulary rows ([256 tokens][68] fp32, 68 KB);
 //  * optionally (u != null) u = exp(z - max) itself, in dz's layout, for the single-sweep
-//    backward (k_rescale_dz turns it into dz once the logsumexp is known).
+//    backward (launch_rescale_dz turns it into dz once the logsumexp is known).
 template <int DT>
 struct EpiFwdLse {
   float2 *part;   // [n_lse][ld] (max, sum exp(z - max)) per wave row of the tile
@@ -529,16 +530,17 @@ struct EpiFwdLse {
 };
 
 // Backward: dz[c][v] = sM[c] * exp(z - lse[c]) for v < V, 0 for V <= v < V_pad.
-// bf16 also writes dzT[v][c] (token-contiguous, for the dW GEMM): lanes c and c ^ 1
-// swap halves of their packed values so that each writes two tokens of two rows.
+// bf16 also writes dzT (token-contiguous in blocks of 256 tokens, for the dW GEMM):
+// lanes c and c ^ 1 swap halves of their packed values so that each writes two tokens
+// of two rows.
 template <int DT>
 struct EpiBwdDz {
   void *dz;      // blocks of 256 vocabulary columns: [V_pad/256][C_alloc][256]
   long long ts;  // C_alloc * 256
   const float *lse, *sM;
   int V, rows, V_pad;
-  unsigned short *dzt;  // [V_pad][ldt] (bf16 only)
-  long long ldt;
+  unsigned short *dzt;  // (v, c) at dzt[(c / 256) * tst + v * 256 + c % 256] (bf16 only)
+  long long tst;
   template <int NRB, int NCB>
   __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
                                              int, char *) const {
@@ -575,9 +577,10 @@ struct EpiBwdDz {
             const unsigned lo = odd ? got : mine, hi = odd ? mine : got;
             const unsigned r0 = (lo & 0xFFFFu) | (hi << 16);
             const unsigned r1 = (lo >> 16) | (hi & 0xFFFF0000u);
-            unsigned short *q = dzt + (long long)(v0 + (odd ? 2 : 0)) * ldt + (c & ~1);
+            unsigned short *q = dzt + (long long)(c >> 8) * tst +
+                                (long long)(v0 + (odd ? 2 : 0)) * 256 + ((c & 255) & ~1);
             *(unsigned *)q = r0;
-            *(unsigned *)(q + ldt) = r1;
+            *(unsigned *)(q + 256) = r1;
           } else {
             *(f32x4 *)((float *)dz + (long long)(v0 >> 8) * ts + c * 256 + (v0 & 255)) =
                 f32x4{x[0], x[1], x[2], x[3]};
@@ -1023,35 +1026,84 @@ hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
 
 // Single-sweep backward: u = exp(z - m_g) from the forward epilogue (m_g the max of the
 // token's group g of gr = tile_rows / 2 vocabulary rows) becomes dz = sM * exp(z - lse) =
-// sM * exp(m_g - lse) * u, in place; bf16 also writes dzT (token-contiguous, zeros for
-// tokens rows <= c < C_alloc).  A block takes 64 vocabulary rows (inside one group, as
-// 64 divides gr) x TC tokens and transposes through LDS.  Each thread first issues all
-// its loads of u (NQ chunks of 8 elements), then the factors are formed.
-template <int DT, int TC>
-__global__ __launch_bounds__(256) void k_rescale_dz(void *dz, long long ts, unsigned short *dzt,
-                                                    long long ldt, const float2 *part,
-                                                    long long ld, const float *lse,
-                                                    const float *sM, int rows, int V, int gr) {
-  constexpr int NQ = TC * 8 / 256;
+// sM * exp(m_g - lse) * u, in place.
+//
+// bf16 also writes dzT, the same values in the token-blocked layout of the dW GEMM's A
+// operand (element (v, c) at dzT[(c / 256) * tst + v * 256 + c % 256], zeros for tokens
+// rows <= c < C_alloc).  A block takes one 256-column block of dz (256 vocabulary rows:
+// two 192-row groups, or three) x TC tokens: the u it reads and rewrites is TC x 512
+// contiguous bytes, and its dzT rows are TC x 2 bytes at a 512-byte pitch.  Each thread
+// first issues all its loads of u (NQ chunks of 8 elements), then the factors are formed.
+// The transpose goes through LDS as [token][256], 16-byte chunk q of token row c stored
+// at q ^ (c / 8 % 32), so that the column reads (8 tokens of one vocabulary row per
+// thread, 16 threads per row) hit distinct banks.
+template <int TC, int NT>
+__global__ __launch_bounds__(NT) void k_rescale_dz_bf16(unsigned short *dz, long long ts,
+                                                        unsigned short *dzt, long long tst,
+                                                        const float2 *part, long long ld,
+                                                        const float *lse, const float *sM,
+                                                        int rows, int V, int gr) {
+  constexpr int NQ = TC * 32 / NT;  // 16-byte chunks per thread
+  static_assert(NQ * NT == TC * 32 && TC % 8 == 0 && 256 % TC == 0, "block shape");
+  __shared__ float f[3][TC];
+  __shared__ __attribute__((aligned(16))) unsigned short t[TC * 256];
+  auto tix = [](int c, int v) { return c * 256 + ((((v >> 3) ^ (c >> 3)) & 31) << 3) + (v & 7); };
+  const int v0 = blockIdx.x * 256, c0 = blockIdx.y * TC, tid = threadIdx.x;
+  unsigned short *ub = dz + (long long)blockIdx.x * ts;  // this column block, [C_alloc][256]
+  u32x4 in[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int q = tid + j * NT, c = c0 + (q >> 5);
+    in[j] = u32x4{0u, 0u, 0u, 0u};
+    if (c < rows) in[j] = *(const u32x4 *)(ub + (long long)c * 256 + (q & 31) * 8);
+  }
+  const int g0 = v0 / gr;  // 256 rows span at most three groups of gr >= 128
+  for (int i = tid; i < 3 * TC; i += NT) {
+    const int gl = i / TC, cl = i - gl * TC, c = c0 + cl, g = g0 + gl;
+    float fc = 0.f;
+    if (c < rows && g * gr < V)
+      fc = sM[c] * fast_exp2((part[(long long)g * ld + c].x - lse[c]) * kLog2e);
+    f[gl][cl] = fc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int q = tid + j * NT, r = q >> 5, vq = (q & 31) * 8, c = c0 + r;
+    const float a = f[(v0 + vq) / gr - g0][r];  // gr is a multiple of 8
+    u32x4 val;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      val[e] = pack_bf16x2(a * bf16_to_f32((unsigned short)(in[j][e] & 0xFFFFu)),
+                           a * bf16_to_f32((unsigned short)(in[j][e] >> 16)));
+    if (c < rows) *(u32x4 *)(ub + (long long)c * 256 + vq) = val;
+    *(u32x4 *)&t[tix(r, vq)] = val;  // zero for c >= rows (a = 0, u = 0)
+  }
+  __syncthreads();
+  unsigned short *tb = dzt + (long long)(c0 >> 8) * tst + (long long)v0 * 256 + (c0 & 255);
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int q = tid + j * NT, vr = q / (TC / 8), c8 = (q % (TC / 8)) * 8;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (unsigned)t[tix(c8 + 2 * e, vr)] | ((unsigned)t[tix(c8 + 2 * e + 1, vr)] << 16);
+    *(u32x4 *)(tb + (long long)vr * 256 + c8) = o;
+  }
+}
+
+// fp32: a block takes 64 vocabulary rows (inside one group, as 64 divides gr) x 64 tokens.
+__global__ __launch_bounds__(256) void k_rescale_dz_f32(float *dz, long long ts, const float2 *part,
+                                                        long long ld, const float *lse,
+                                                        const float *sM, int rows, int V, int gr) {
+  constexpr int TC = 64, NQ = TC * 8 / 256;
   __shared__ float f[TC];
-  // [TC tokens][64 rows], 16-B chunks of a token's row XOR-swizzled by token / 8 so that
-  // the column reads of the transpose hit at most two tokens per bank
-  __shared__ __attribute__((aligned(16))) unsigned short t[DT == 1 ? TC * 64 : 8];
-  auto tix = [](int c, int v) { return c * 64 + ((((v >> 3) ^ (c >> 3)) & 7) << 3) + (v & 7); };
   const int v0 = blockIdx.x * 64, c0 = blockIdx.y * TC, tid = threadIdx.x;
-  using Chunk = typename std::conditional<DT == 1, u32x4, f32x8>::type;
-  Chunk in[NQ];
+  f32x8 in[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int q = tid + j * 256, r = q >> 3, v = v0 + (q & 7) * 8, c = c0 + r;
-    in[j] = Chunk{};
-    if (c < rows) {
-      const long long o = (long long)(v >> 8) * ts + c * 256 + (v & 255);
-      if constexpr (DT == 1)
-        in[j] = *(const u32x4 *)((const unsigned short *)dz + o);
-      else
-        in[j] = *(const f32x8 *)((const float *)dz + o);
-    }
+    in[j] = f32x8{};
+    if (c < rows) in[j] = *(const f32x8 *)(dz + (long long)(v >> 8) * ts + c * 256 + (v & 255));
   }
   if (tid < TC) {
     const int c = c0 + tid;
@@ -1063,66 +1115,43 @@ __global__ __launch_bounds__(256) void k_rescale_dz(void *dz, long long ts, unsi
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    const int q = tid + j * 256, r = q >> 3, v8 = (q & 7) * 8, v = v0 + v8, c = c0 + r;
-    const float a = f[r];
-    const long long o = (long long)(v >> 8) * ts + c * 256 + (v & 255);
-    if constexpr (DT == 1) {
-      u32x4 val;
+    const int q = tid + j * 256, r = q >> 3, v = v0 + (q & 7) * 8, c = c0 + r;
+    if (c >= rows) continue;
+    f32x8 x = in[j];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        val[e] = pack_bf16x2(a * bf16_to_f32((unsigned short)(in[j][e] & 0xFFFFu)),
-                             a * bf16_to_f32((unsigned short)(in[j][e] >> 16)));
-      if (c < rows) *(u32x4 *)((unsigned short *)dz + o) = val;
-      *(u32x4 *)&t[tix(r, v8)] = val;  // zero for c >= rows (a = 0, u = 0)
-    } else {
-      if (c < rows) {
-        f32x8 x = in[j];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= a;
-        *(f32x8 *)((float *)dz + o) = x;
-      }
-    }
-  }
-  if constexpr (DT == 1) {
-    __syncthreads();
-    // dzT: 64 rows of TC tokens, 16 B per lane
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int q = tid + j * 256, vr = q / (TC / 8), c8 = (q % (TC / 8)) * 8;
-      u32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        o[e] = (unsigned)t[tix(c8 + 2 * e, vr)] | ((unsigned)t[tix(c8 + 2 * e + 1, vr)] << 16);
-      *(u32x4 *)(dzt + (long long)(v0 + vr) * ldt + c0 + c8) = o;
-    }
+    for (int e = 0; e < 8; ++e) x[e] *= f[r];
+    *(f32x8 *)(dz + (long long)(v >> 8) * ts + c * 256 + (v & 255)) = x;
   }
 }
 
-hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, int64_t ldt, const float2 *partials,
+constexpr int kRescTC = 128, kRescNT = 256;  // bf16 rescale block: tokens, threads
+
+hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, int64_t tst, const float2 *partials,
                              const float *lse, const float *sM, int64_t rows, int64_t V,
                              int64_t V_pad, int64_t C_alloc, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (dtype == 1)  // C_alloc is a multiple of 256
-    hipLaunchKernelGGL((k_rescale_dz<1, 128>), dim3((unsigned)(V_pad / 64), (unsigned)(C_alloc / 128)),
-                       dim3(256), 0, s, dz, (long long)C_alloc * 256, (unsigned short *)dzt,
-                       (long long)ldt, partials, (long long)C_alloc, lse, sM, (int)rows, (int)V,
+  if (dtype == 1)  // C_alloc and V_pad are multiples of 256
+    hipLaunchKernelGGL((k_rescale_dz_bf16<kRescTC, kRescNT>),
+                       dim3((unsigned)(V_pad / 256), (unsigned)(C_alloc / kRescTC)), dim3(kRescNT),
+                       0, s, (unsigned short *)dz, (long long)C_alloc * 256, (unsigned short *)dzt,
+                       (long long)tst, partials, (long long)C_alloc, lse, sM, (int)rows, (int)V,
                        tile_rows(1) / 2);
   else
-    hipLaunchKernelGGL((k_rescale_dz<0, 64>), dim3((unsigned)(V_pad / 64), (unsigned)(C_alloc / 64)),
-                       dim3(256), 0, s, dz, (long long)C_alloc * 256, (unsigned short *)nullptr, 0LL,
-                       partials, (long long)C_alloc, lse, sM, (int)rows, (int)V, tile_rows(0) / 2);
+    hipLaunchKernelGGL(k_rescale_dz_f32, dim3((unsigned)(V_pad / 64), (unsigned)(C_alloc / 64)),
+                       dim3(256), 0, s, (float *)dz, (long long)C_alloc * 256, partials,
+                       (long long)C_alloc, lse, sM, (int)rows, (int)V, tile_rows(0) / 2);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t rows, int64_t d,
                            int64_t V, const float *lse, const float *sM, void *dz, void *dzt,
-                           int64_t ldt, int64_t V_pad, int64_t C_alloc, hipStream_t s) {
+                           int64_t tst, int64_t V_pad, int64_t C_alloc, hipStream_t s) {
   Operand A{W, d, (int)V, (int)d, 256};
   Operand B{h_c, d, (int)rows, (int)d, 256};
   GemmGrid G{(int)(V_pad / tile_rows(dtype)), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
   if (dtype == 1) {
     EpiBwdDz<1> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows, (int)V_pad,
-                  (unsigned short *)dzt, ldt};
+                  (unsigned short *)dzt, tst};
     return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
   }
   EpiBwdDz<0> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows, (int)V_pad, nullptr, 0};
@@ -1184,16 +1213,17 @@ hipError_t launch_transpose_w(const void *W, int64_t V, int64_t d, int64_t V_pad
 }
 
 hipError_t launch_dw_gemm(int dtype, const void *dz, const void *dzt, const void *h_c,
-                          const void *ht, int64_t ldt, int64_t k, int64_t d, int64_t V,
+                          const void *ht, int64_t k, int64_t d, int64_t V,
                           int64_t V_pad, int64_t C_alloc, float *dW, int accumulate,
                           hipStream_t s) {
   // D[v][j] = sum_c dz[c][v] h[c][j] over k tokens
   GemmGrid G{cdiv(V, tile_rows(dtype)), cdiv(d, kTile), 1, (int)k, (int)k, 0};
   EpiDw e{dW, (int)d, (int)V, accumulate};
   if (dtype == 1) {
-    // A = dzT ([v][c]), B = hT ([j][c]): both token-contiguous (KC)
-    Operand A{dzt, ldt, (int)V, (int)k, 256};
-    Operand B{ht, ldt, (int)d, (int)k, 256};
+    // A = dzT ([v][c]), B = hT ([j][c]): both token-contiguous (KC), in blocks of 256
+    // tokens ([V_pad][256] and [d][256] each)
+    Operand A{dzt, 256, (int)V, (int)k, V_pad * 256};
+    Operand B{ht, 256, (int)d, (int)k, d * 256};
     return run_gemm<1, OP_KC, OP_KC>(A, B, G, e, s);
   }
   // A = dz as MC ([c][v] in 256-column blocks), B = h as MC ([c][j])
@@ -1202,10 +1232,11 @@ hipError_t launch_dw_gemm(int dtype, const void *dz, const void *dzt, const void
   return run_gemm<0, OP_MC, OP_MC>(A, B, G, e, s);
 }
 
-// h chunk [rows][d] -> hT [d][ldt] (bf16), columns c < ncols (zero for c >= rows), through
-// a 64 x 64 LDS tile.
+// h chunk [rows][d] -> hT (bf16), token-contiguous in blocks of 256 tokens: element (j, c)
+// at ht[(c / 256) * tst + j * 256 + c % 256], columns c < ncols (zero for c >= rows),
+// through a 64 x 64 LDS tile.
 __global__ __launch_bounds__(256) void k_transpose_h(const unsigned short *h, int rows, int ncols,
-                                                     int d, long long ldt, unsigned short *ht) {
+                                                     int d, long long tst, unsigned short *ht) {
   __shared__ __attribute__((aligned(16))) unsigned short t[64][72];
   const int c0 = blockIdx.x * 64, j0 = blockIdx.y * 64, tid = threadIdx.x;
 #pragma unroll
@@ -1226,16 +1257,16 @@ __global__ __launch_bounds__(256) void k_transpose_h(const unsigned short *h, in
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       o[e] = (unsigned)t[c8 + 2 * e][jr] | ((unsigned)t[c8 + 2 * e + 1][jr] << 16);
-    *(u32x4 *)(ht + (long long)j * ldt + c) = o;  // ncols % 8 == 0
+    *(u32x4 *)(ht + (long long)(c >> 8) * tst + (long long)j * 256 + (c & 255)) = o;  // ncols % 8 == 0
   }
 }
 
 hipError_t launch_transpose_h(const void *h_c, int64_t rows, int64_t d, int64_t C_alloc,
-                              void *ht, int64_t ldt, hipStream_t s) {
+                              void *ht, int64_t tst, hipStream_t s) {
   if (C_alloc <= 0) return hipSuccess;
   const dim3 grid((unsigned)(C_alloc / 64), (unsigned)((d + 63) / 64));
   hipLaunchKernelGGL(k_transpose_h, grid, dim3(256), 0, s, (const unsigned short *)h_c, (int)rows,
-                     (int)C_alloc, (int)d, (long long)ldt, (unsigned short *)ht);
+                     (int)C_alloc, (int)d, (long long)tst, (unsigned short *)ht);
   return hipGetLastError();
 }
 
@@ -1561,7 +1592,7 @@ hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStr
 // threads touch the same element.
 template <int DT>
 __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigned short *dzt,
-                                                 long long ldt, const int32_t *idx,
+                                                 long long tst, const int32_t *idx,
                                                  const float *p, const float *srow, int rows,
                                                  int K) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1596,7 +1627,7 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigne
       unsigned short *q = (unsigned short *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
       const unsigned short nv = f32_to_bf16(bf16_to_f32(*q) - sr * tot);
       *q = nv;
-      dzt[(long long)v * ldt + r] = nv;
+      dzt[(long long)(r >> 8) * tst + (long long)v * 256 + (r & 255)] = nv;
     } else {
       float *q = (float *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
       *q = *q - sr * tot;
@@ -1604,13 +1635,13 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigne
   }
 }
 
-hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t ldt, int64_t C_alloc,
+hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t tst, int64_t C_alloc,
                           const int32_t *idx_c, const float *p_c, const float *srow, int64_t rows,
                           int32_t K, hipStream_t s) {
   const int blocks = (int)((rows + 3) / 4);
   if (dtype == 1)
     hipLaunchKernelGGL(k_scatter<1>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256,
-                       (unsigned short *)dzt, (long long)ldt, idx_c, p_c, srow, (int)rows,
+                       (unsigned short *)dzt, (long long)tst, idx_c, p_c, srow, (int)rows,
                        (int)K);
   else
     hipLaunchKernelGGL(k_scatter<0>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256,

@@ -47,9 +47,9 @@ def test_workspace_is_independent_of_N_beyond_one_chunk(lib):
     c = kd.workspace_bytes(4096, 3072, 128256, 100, 2048)
     assert a == b == c
     assert a % 256 == 0
-    # one chunk's dz, the token-contiguous dz of a 4096-token dW group (bf16) and W^T
+    # one chunk's dz, the token-contiguous dz of an 8192-token dW group (bf16) and W^T
     # dominate; no N x V term
-    dz, dzt, wt = 2048 * 128256 * 2, 4096 * 128256 * 2, 128256 * 3072 * 2
+    dz, dzt, wt = 2048 * 128256 * 2, 8192 * 128256 * 2, 128256 * 3072 * 2
     assert dz + dzt + wt < a < dz + dzt + wt + 600_000_000
     small = kd.workspace_bytes(100, 3072, 128256, 100, 2048)
     assert small < a
