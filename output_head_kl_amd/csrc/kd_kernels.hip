@@ -467,7 +467,17 @@ struct EpiFwdLse {
         (LDS_AS unsigned short *)smem + (threadIdx.x >> 6) * TOK * PITCH;
     const int vl = m0 + (lane >> 5) * 4;
     const bool live = m0 < V;                 // the wave has rows below V
-    const bool full = m0 + WR <= V;
+    if (live && m0 + WR > V) {
+      // rows v >= V of the last vocabulary tile drop out of the max and the sum as -inf
+      // (exp2(-inf) = 0), so that whole waves need no per-element bound test below
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (vl + rb * 32 + (i >> 2) * 8 + (i & 3) >= V) acc[rb][cb][i] = -INFINITY;
+    }
     float mx[NCB], sum[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -475,11 +485,10 @@ struct EpiFwdLse {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = vl + rb * 32 + (i >> 2) * 8 + (i & 3);
-          if (full || v < V) m = fmaxf(m, acc[rb][cb][i]);
-        }
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[rb][cb][i]);
       mx[cb] = halves_max(m);
+      // a wave wholly past V: every u is 0 (and the max stays -inf, so avoid inf - inf)
+      if (!live) mx[cb] = INFINITY;
       sum[cb] = 0.f;
     }
 #pragma unroll
@@ -493,13 +502,10 @@ struct EpiFwdLse {
           const int rb = p * RP + r;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int v0 = vl + rb * 32 + g * 8;
             float x[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              x[e] = live && (full || v0 + e < V)
-                         ? fast_exp2(fmaf(acc[rb][cb][g * 4 + e], kLog2e, -mx2))
-                         : 0.f;
+              x[e] = fast_exp2(fmaf(acc[rb][cb][g * 4 + e], kLog2e, -mx2));
               sum[cb] += x[e];
             }
             if (keep) {
@@ -687,6 +693,7 @@ struct EpiDw {
 // ---------------------------------------------------------------------------------
 namespace pipe {
 constexpr int OOB = (int)0x80000000;   // offset outside every buffer: reads zero
+constexpr int kLoadSc1 = 16;           // buffer-load cache-policy bit SC1
 
 // Stage geometry for a k-depth of BK bf16 (32 or 64) and ROWS tile rows (256 or 384).
 template <int BK, int ROWS = 256> struct Geo {
@@ -761,8 +768,11 @@ static __device__ __forceinline__ void issue(const Operand &op, const LaneChunks
     int mn, k, off;
     c.at(w * NI + j, mn, k, off);
     const bool ok = (mn0 + mn < op.mn_ext) && (k0 + k < op.k_ext);
+    // cache policy sc1 (device scope): the operand lines go through L2 only; each CU reads
+    // a line once per stage, so the vector L1 holds nothing it would reuse
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (LDS_AS void *)((LDS_AS char *)lds + (w * NI + j) * 1024), 16, ok ? off : OOB, 0, 0, 0);
+        rs, (LDS_AS void *)((LDS_AS char *)lds + (w * NI + j) * 1024), 16, ok ? off : OOB, 0, 0,
+        kLoadSc1);
   }
 }
 };
