@@ -341,39 +341,55 @@ struct EpiFwdLse {
                                              int, char *smem) const {
     constexpr int WR = 32 * NRB, TR = 2 * WR, SPW = WR / 64;  // slices of 64 rows per wave row
     // Fused gather first, while no other temporaries are live (the same branch for every
-    // wave of the workgroup).
+    // wave of the workgroup).  The tile's z goes through LDS SPP slices of 64 vocabulary
+    // rows at a time ([256 tokens][68] fp32 each, 68 KB); when the tile has at most one
+    // hit per thread, each thread loads its entry once and keeps it for every pass.
     const int tm = m0 / TR, tn = n0 >> 8;
     const int key = tm * ntn + tn;
     const int beg = boff[key], end = boff[key + 1];
     if (beg != end) {
       const int t = threadIdx.x, wr = (m0 - tm * TR) / WR;
-      constexpr int P = 68;
+      constexpr int P = 68, SLB = 256 * P * 4;      // slice pitch (floats), slice bytes
+      constexpr int NS = 2 * SPW;                   // 64-row slices in the tile
+      constexpr int SPP = DT == 1 ? 2 : 1;          // slices per pass (bf16 core: 160 KB LDS)
+      static_assert(NS % SPP == 0, "whole passes");
       const int cl0 = (n0 & 255) + (lane & 31);
+      const bool one = end - beg <= (int)blockDim.x;
+      const unsigned ent1 = one && beg + t < end ? bent[beg + t] : 0xFFFFFFFFu;
 #pragma unroll
-      for (int q = 0; q < 2 * SPW; ++q) {
+      for (int q = 0; q < NS / SPP; ++q) {
         __syncthreads();
-        if (wr == q / SPW) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int rb = (q % SPW) * 2 + h;
+        for (int hs = 0; hs < SPP; ++hs) {
+          const int sl = q * SPP + hs;
+          if (wr == sl / SPW) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
+            for (int h = 0; h < 2; ++h) {
+              const int rb = (sl % SPW) * 2 + h;
 #pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const int vloc = h * 32 + g * 8 + (lane >> 5) * 4;
-                const f32x4 v4 = {acc[rb][cb][g * 4], acc[rb][cb][g * 4 + 1], acc[rb][cb][g * 4 + 2],
-                                  acc[rb][cb][g * 4 + 3]};
-                *(LDS_AS f32x4 *)((LDS_AS char *)smem + ((cl0 + cb * 32) * P + vloc) * 4) = v4;
-              }
+              for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  const int vloc = h * 32 + g * 8 + (lane >> 5) * 4;
+                  const f32x4 v4 = {acc[rb][cb][g * 4], acc[rb][cb][g * 4 + 1],
+                                    acc[rb][cb][g * 4 + 2], acc[rb][cb][g * 4 + 3]};
+                  *(LDS_AS f32x4 *)((LDS_AS char *)smem + hs * SLB +
+                                    ((cl0 + cb * 32) * P + vloc) * 4) = v4;
+                }
+            }
           }
         }
         __syncthreads();
-        for (int e = beg + t; e < end; e += blockDim.x) {
-          const unsigned ent = bent[e];
+        auto take = [&](unsigned ent) {
           const int cl = ent & 255, vloc = (ent >> 8) & 511, k = ent >> 17;
-          if ((vloc >> 6) == q)
-            zg[(long long)(tn * 256 + cl) * K + k] =
-                *(const LDS_AS float *)((const LDS_AS char *)smem + (cl * P + (vloc & 63)) * 4);
+          if ((vloc >> 6) / SPP == q)
+            zg[(long long)(tn * 256 + cl) * K + k] = *(const LDS_AS float *)(
+                (const LDS_AS char *)smem + ((vloc >> 6) % SPP) * SLB + (cl * P + (vloc & 63)) * 4);
+        };
+        if (one) {
+          if (ent1 != 0xFFFFFFFFu) take(ent1);
+        } else {
+          for (int e = beg + t; e < end; e += blockDim.x) take(bent[e]);
         }
       }
     }
