@@ -325,6 +325,7 @@ void gemm_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
 //    backward (launch_rescale_dz turns it into dz once the logsumexp is known).
 template <int DT>
 struct EpiFwdLse {
+  static constexpr bool kPrefetch = true;
   float2 *part;   // [n_lse][ld] (max, sum exp(z - max)) per wave row of the tile
   long long ld;
   int V, rows;
@@ -336,17 +337,40 @@ struct EpiFwdLse {
   void *u;                // null, or dz's buffer: [V_pad/256][C_alloc][256]
   long long ts;           // C_alloc * 256
   int V_pad;
+  // The tile's bucket of teacher hits: [beg, end) of the entries, and when the tile has
+  // at most one hit per thread, this thread's entry (else ~0).  The pipelined core loads
+  // it before its k-loop, so that the loads' latency hides behind the loop.
+  struct Pre {
+    int beg, end;
+    unsigned ent1;
+  };
+  template <int NRB>
+  __device__ __forceinline__ Pre prefetch(int m0, int n0) const {
+    constexpr int TR = 64 * NRB;
+    const int key = (m0 / TR) * ntn + (n0 >> 8);
+    Pre pr;
+    pr.beg = boff[key];
+    pr.end = boff[key + 1];
+    const int t = threadIdx.x;
+    pr.ent1 = pr.end - pr.beg <= (int)blockDim.x && pr.beg + t < pr.end ? bent[pr.beg + t]
+                                                                          : 0xFFFFFFFFu;
+    return pr;
+  }
   template <int NRB, int NCB>
   __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
-                                             int, char *smem) const {
+                                             int split, char *smem) const {
+    (*this)(acc, m0, n0, lane, split, smem, prefetch<NRB>(m0, n0));
+  }
+  template <int NRB, int NCB>
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
+                                             int, char *smem, const Pre &pr) const {
     constexpr int WR = 32 * NRB, TR = 2 * WR, SPW = WR / 64;  // slices of 64 rows per wave row
     // Fused gather first, while no other temporaries are live (the same branch for every
     // wave of the workgroup).  The tile's z goes through LDS SPP slices of 64 vocabulary
     // rows at a time ([256 tokens][68] fp32 each, 68 KB); when the tile has at most one
-    // hit per thread, each thread loads its entry once and keeps it for every pass.
+    // hit per thread, each thread's entry was loaded once (prefetch) for every pass.
     const int tm = m0 / TR, tn = n0 >> 8;
-    const int key = tm * ntn + tn;
-    const int beg = boff[key], end = boff[key + 1];
+    const int beg = pr.beg, end = pr.end;
     if (beg != end) {
       const int t = threadIdx.x, wr = (m0 - tm * TR) / WR;
       constexpr int P = 68, SLB = 256 * P * 4;      // slice pitch (floats), slice bytes
@@ -355,7 +379,7 @@ struct EpiFwdLse {
       static_assert(NS % SPP == 0, "whole passes");
       const int cl0 = (n0 & 255) + (lane & 31);
       const bool one = end - beg <= (int)blockDim.x;
-      const unsigned ent1 = one && beg + t < end ? bent[beg + t] : 0xFFFFFFFFu;
+      const unsigned ent1 = pr.ent1;
 #pragma unroll
       for (int q = 0; q < NS / SPP; ++q) {
         __syncthreads();
@@ -557,6 +581,8 @@ struct EpiFwdLse {
 // of two rows.
 template <int DT>
 struct EpiBwdDz {
+  static constexpr bool kPrefetch = false;
+  struct Pre {};
   void *dz;      // blocks of 256 vocabulary columns: [V_pad/256][C_alloc][256]
   long long ts;  // C_alloc * 256
   const float *lse, *sM;
@@ -614,6 +640,8 @@ struct EpiBwdDz {
 
 // dh split: tile rows are hidden units j, columns tokens c; fp32 partial per split.
 struct EpiDhPart {
+  static constexpr bool kPrefetch = false;
+  struct Pre {};
   float *part;
   long long split_stride, ld;  // C_alloc*d_pad, d_pad
   int rows;
@@ -646,6 +674,8 @@ struct EpiDhPart {
 // workgroup does not wait for dW to be read back and the result does not depend on
 // timing (each element gets exactly one addition per launch, launches are ordered).
 struct EpiDw {
+  static constexpr bool kPrefetch = false;
+  struct Pre {};
   float *dW;
   int d, V, accumulate;
   template <int NRB, int NCB>
@@ -909,6 +939,9 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
     Loader<AK, BK, NIA>::issue(Ak, ca, m0, kb + s * BK, smem + s * GA::OPB, w);
     if (s < NSTB) Loader<BKIND, BK, NIB>::issue(Bk, cb, n0, kb + s * BK, smemB + s * GB::OPB, w);
   }
+  // epilogue inputs that do not depend on the product, loaded behind the first stages
+  typename Epi::Pre pre{};
+  if constexpr (Epi::kPrefetch) pre = epi.template prefetch<NRB>(m0 + wr * WMR, n0 + wc * WNC);
   wait_vm<NIA * (NSTA - 1) + NIB * (NSTB - 1), false>();
   __syncthreads();
 
@@ -1008,7 +1041,10 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
     bcur = bnext;
   }
   wait_vm<0, false>();  // the zero loads issued past the end
-  epi(acc, m0 + wr * WMR, n0 + wc * WNC, lane, split, smem);
+  if constexpr (Epi::kPrefetch)
+    epi(acc, m0 + wr * WMR, n0 + wc * WNC, lane, split, smem, pre);
+  else
+    epi(acc, m0 + wr * WMR, n0 + wc * WNC, lane, split, smem);
 }
 
 template <int DT, int AK, int BKIND, class Epi>
