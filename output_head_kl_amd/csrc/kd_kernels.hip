@@ -802,11 +802,35 @@ template <int KIND, int BK, int NI> struct LaneChunks {
   }
 };
 
+// Cache policy sc1 (device scope) on every operand load: the lines go through L2 only;
+// each CU reads a line once per stage, so the vector L1 holds nothing it would reuse.
 template <int KIND, int BK, int NI> struct Loader {
 static __device__ __forceinline__ void issue(const Operand &op, const LaneChunks<KIND, BK, NI> &c,
                                              int mn0, int k0, char *lds, int w) {
   const unsigned short *base = (const unsigned short *)op.ptr;
   base += op_index(op, KIND, mn0, k0);   // a stage never crosses a 256-column block
+  if (KIND == OP_KC && k0 + BK <= op.k_ext) {
+    // The whole stage lies inside k.  The resource ends at row mn_ext, so the hardware
+    // drops rows past the operand; chunk g = w*NI + j (rows 8g .. 8g+7 of the tile) is at
+    // rel[g & 1] + 16 g ld bytes.  The two lane offsets are made opaque here so that the
+    // per-chunk offsets are formed at each stage instead of being held in registers.
+    const long long rows = (long long)op.mn_ext - mn0;
+    const long long bytes = rows * op.ld * 2;
+    const int nrec = rows <= 0 ? 0 : bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, nrec, 0x00020000);
+    int r0 = c.rel[0], r1 = c.rel[1];
+    asm volatile("" : "+v"(r0), "+v"(r1));
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int g = w * NI + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (LDS_AS void *)((LDS_AS char *)lds + g * 1024), 16,
+          ((j & 1) ? r1 : r0) + (int)(16LL * g * op.ld), 0, 0, kLoadSc1);
+    }
+    return;
+  }
+  // general case (the last, partial stage of k, or an MC operand): per-lane tests
   __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
@@ -814,8 +838,6 @@ static __device__ __forceinline__ void issue(const Operand &op, const LaneChunks
     int mn, k, off;
     c.at(w * NI + j, mn, k, off);
     const bool ok = (mn0 + mn < op.mn_ext) && (k0 + k < op.k_ext);
-    // cache policy sc1 (device scope): the operand lines go through L2 only; each CU reads
-    // a line once per stage, so the vector L1 holds nothing it would reuse
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (LDS_AS void *)((LDS_AS char *)lds + (w * NI + j) * 1024), 16, ok ? off : OOB, 0, 0,
         kLoadSc1);
