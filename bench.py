@@ -33,8 +33,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload id (synth.CONFIGS)")
     ap.add_argument("--N", type=int, default=None, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512,
-                    help="token rows of the workload timed through the CPU oracle")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="token rows of the workload timed through the CPU oracle (a bounded "
+                         "sample: ~15-25 s of host time at the full vocabulary)")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip per-kernel HIP-event timing inside the timed region")
     ap.add_argument("--split", action="store_true",
@@ -296,15 +297,29 @@ def memory_sweep():
         print(f"[memory] N={N}: peak {peaks[-1] / 2**30:.3f} GiB, free drop "
               f"{(free0 - free1) / 2**20:.1f} MiB, reserved growth {(res1 - res0) / 2**20:.1f} MiB",
               file=sys.stderr, flush=True)
+    def linfit(x, y):
+        b, a = np.polyfit(x, y, 1)
+        fit = a + b * x
+        r2 = 1.0 - np.sum((y - fit) ** 2) / np.sum((y - y.mean()) ** 2)
+        return a, b, r2, float(np.abs(y - fit).max())
+
+    # The workspace grows with N only until the dW group (16384 tokens) is full, then
+    # stays constant: fit peak(N) over the points past that, and peak minus workspace
+    # over all of them.
     x = np.array(Ns, dtype=np.float64)
     y = np.array(peaks, dtype=np.float64)
-    b, a = np.polyfit(x, y, 1)
-    fit = a + b * x
-    r2 = 1.0 - np.sum((y - fit) ** 2) / np.sum((y - y.mean()) ** 2)
+    ws = np.array([r["workspace_bytes"] for r in rows], dtype=np.float64)
+    full = ws == ws.max()
+    a, b, r2, resid = linfit(x[full], y[full])
+    a2, b2, r22, resid2 = linfit(x, y - ws)
     res = {"memory_sweep": {"d": d, "V": V, "K": K, "chunk": chunk, "dtype": "bf16",
                             "W_bytes": V * d * 2, "allocated_before_sweep_bytes": base,
+                            "fit_from_N": int(x[full].min()),
                             "fit_intercept_bytes": a, "fit_bytes_per_token": b, "r2": r2,
-                            "max_abs_residual_bytes": float(np.abs(y - fit).max()),
+                            "max_abs_residual_bytes": resid,
+                            "fit_without_workspace": {"intercept_bytes": a2,
+                                                      "bytes_per_token": b2, "r2": r22,
+                                                      "max_abs_residual_bytes": resid2},
                             "points": rows}}
     print(json.dumps(res), flush=True)
 

@@ -141,8 +141,11 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->off_bent = take((size_t)L->C_alloc * K * 4);
   L->off_wt = take(dtype == KD_BF16 ? (size_t)L->V_pad * d * 2 : 0);
   L->off_idxloc = take((size_t)L->C_alloc * K * 4);
-  L->dw_group = dtype == KD_BF16 && L->C_alloc < kDwGroupTokens
-                    ? (int)(kDwGroupTokens / L->C_alloc) : 1;
+  {
+    const int64_t nchunks = (Nn + L->C - 1) / L->C;
+    int64_t g = dtype == KD_BF16 && L->C_alloc < kDwGroupTokens ? kDwGroupTokens / L->C_alloc : 1;
+    L->dw_group = (int)(g < nchunks ? g : nchunks);
+  }
   L->off_dzt = take(dtype == KD_BF16 ? (size_t)L->V_pad * L->dw_group * L->C_alloc * 2 : 0);
   L->off_ht = take(dtype == KD_BF16 ? (size_t)d * L->dw_group * L->C_alloc * 2 : 0);
   L->total = off;

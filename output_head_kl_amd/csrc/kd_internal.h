@@ -17,8 +17,9 @@ constexpr int kTile = 256;
 constexpr int kTileA16 = 384;
 inline int tile_rows(int dtype) { return dtype == 1 ? kTileA16 : kTile; }
 // Tokens per dW GEMM launch (bf16): each launch adds its product into the fp32 dW, a
-// read and a write of all of dW, so chunks are grouped up to this many tokens.
-constexpr int kDwGroupTokens = 8192;
+// read and a write of all of dW, so chunks are grouped up to this many tokens (and never
+// more chunks than the batch has).
+constexpr int kDwGroupTokens = 16384;
 
 // Kernel classes for timing (kd_profile_*).
 enum KClass {

@@ -492,7 +492,8 @@ struct EpiFwdLse {
 
   // bf16, 192-row waves: as above, but u (when wanted) goes out through LDS so that the
   // stores are whole 16-byte pieces of a token's vocabulary run (192 contiguous bytes
-  // per token and pass) instead of 8-byte pieces for 32 tokens at once.  Each wave
+  // per token and pass) instead of 8-byte pieces for 32 tokens at once.  They are
+  // non-temporal: u is streamed once into the rescale, and the GEMM's operands keep L2.  Each wave
   // stages its own 96 rows x 32*NCB tokens per pass in a private slice of LDS (13 KB);
   // the workgroup barrier first lets every wave finish with the gather's staging buffer.
   template <int NRB, int NCB>
@@ -562,7 +563,8 @@ struct EpiFwdLse {
         const int c = n0 + cl, v = m0 + p * RP * 32 + pc * 8;
         const u32x4 val = *(const LDS_AS u32x4 *)(stg + cl * PITCH + pc * 8);
         if (c < rows)
-          *(u32x4 *)((unsigned short *)u + (long long)(v >> 8) * ts + c * 256 + (v & 255)) = val;
+          __builtin_nontemporal_store(
+              val, (u32x4 *)((unsigned short *)u + (long long)(v >> 8) * ts + c * 256 + (v & 255)));
       }
     }
     if (!live) return;
@@ -1163,6 +1165,8 @@ __global__ __launch_bounds__(NT) void k_rescale_dz_bf16(unsigned short *dz, long
     *(u32x4 *)&t[tix(r, vq)] = val;  // zero for c >= rows (a = 0, u = 0)
   }
   __syncthreads();
+  // dzT is read only by the dW GEMM, after the rest of its group: streamed out with
+  // non-temporal stores, so that it does not displace the operands of the kernels between
   unsigned short *tb = dzt + (long long)(c0 >> 8) * tst + (long long)v0 * 256 + (c0 & 255);
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
@@ -1171,7 +1175,7 @@ __global__ __launch_bounds__(NT) void k_rescale_dz_bf16(unsigned short *dz, long
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       o[e] = (unsigned)t[tix(c8 + 2 * e, vr)] | ((unsigned)t[tix(c8 + 2 * e + 1, vr)] << 16);
-    *(u32x4 *)(tb + (long long)vr * 256 + c8) = o;
+    __builtin_nontemporal_store(o, (u32x4 *)(tb + (long long)vr * 256 + c8));
   }
 }
 

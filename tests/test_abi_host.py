@@ -41,18 +41,26 @@ def test_version_and_profile_classes(lib):
     assert "fwd_gemm_lse" in names and "dw_gemm" in names and len(names) == len(set(names))
 
 
-def test_workspace_is_independent_of_N_beyond_one_chunk(lib):
+def test_workspace_is_bounded_and_constant_beyond_one_dw_group(lib):
+    """The workspace holds one chunk's dz and a dW group of at most 16384 tokens (never
+    more chunks than the batch has): constant in N from there on, with no N x V term."""
     a = kd.workspace_bytes(32768, 3072, 128256, 100, 2048)
     b = kd.workspace_bytes(262144, 3072, 128256, 100, 2048)
-    c = kd.workspace_bytes(4096, 3072, 128256, 100, 2048)
+    c = kd.workspace_bytes(16384, 3072, 128256, 100, 2048)
     assert a == b == c
     assert a % 256 == 0
-    # one chunk's dz, the token-contiguous dz of an 8192-token dW group (bf16) and W^T
-    # dominate; no N x V term
-    dz, dzt, wt = 2048 * 128256 * 2, 8192 * 128256 * 2, 128256 * 3072 * 2
+    # one chunk's dz, the token-contiguous dz of a 16384-token dW group (bf16) and W^T
+    # dominate
+    dz, dzt, wt = 2048 * 128256 * 2, 16384 * 128256 * 2, 128256 * 3072 * 2
     assert dz + dzt + wt < a < dz + dzt + wt + 600_000_000
+    # smaller batches get a smaller dW group: two 2048-token chunks at N = 4096
+    d = kd.workspace_bytes(4096, 3072, 128256, 100, 2048)
+    assert d == a - (16384 - 4096) * 128256 * 2 - (16384 - 4096) * 3072 * 2
     small = kd.workspace_bytes(100, 3072, 128256, 100, 2048)
-    assert small < a
+    assert small < d < a
+    # sizes never decrease with N
+    sizes = [kd.workspace_bytes(n, 3072, 128256, 100, 2048) for n in (1, 2048, 2049, 8192, 20000)]
+    assert sizes == sorted(sizes)
 
 
 @pytest.mark.parametrize("args,code", [
