@@ -593,7 +593,11 @@ struct EpiBwdDz {
   long long tst;
   template <int NRB, int NCB>
   __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
-                                             int, char *) const {
+                                             int, char *smem) const {
+    if constexpr (DT == 1 && NRB % 3 == 0) {
+      staged(acc, m0, n0, lane, smem);
+      return;
+    }
     const int vl = m0 + (lane >> 5) * 4;
     const bool odd = lane & 1;
 #pragma unroll
@@ -636,6 +640,82 @@ struct EpiBwdDz {
                 f32x4{x[0], x[1], x[2], x[3]};
           }
         }
+    }
+  }
+
+  // bf16, 192-row waves: dz and dzT leave through a per-wave LDS slice ([64 tokens][96
+  // rows] per pass, 13 KB), dz as 16-byte pieces of each token's 96-row run, dzT as
+  // 16-byte pieces (8 tokens) of each row's 64-token run, instead of 8-byte and 4-byte
+  // scattered stores.  dzT is read only by the group's dW GEMM: non-temporal stores.
+  template <int NRB, int NCB>
+  __device__ __forceinline__ void staged(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
+                                         char *smem) const {
+    constexpr int RP = 3, NP = NRB / RP;                 // 32-row blocks per pass, passes
+    constexpr int TOK = 32 * NCB, PITCH = 104;           // tokens per wave, bf16 per row
+    constexpr int QPR = RP * 32 / 8;                     // 16-byte pieces per token row
+    constexpr int TG = TOK / 8;                          // 8-token groups per vocabulary row
+    __syncthreads();  // every wave is done with the k-loop's LDS ring
+    LDS_AS unsigned short *stg =
+        (LDS_AS unsigned short *)smem + (threadIdx.x >> 6) * TOK * PITCH;
+    const int vl = m0 + (lane >> 5) * 4;
+    float l2[NCB], a[NCB];
+    bool cv[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      // tokens rows <= c < C_alloc get zeros: the dW GEMM reads dzT in 8-token chunks
+      const int c = n0 + cb * 32 + (lane & 31);
+      cv[cb] = c < rows;
+      l2[cb] = cv[cb] ? lse[c] * kLog2e : 0.f;
+      a[cb] = cv[cb] ? sM[c] : 0.f;
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int cl = cb * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          const int rb = p * RP + r;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int v0 = vl + rb * 32 + g * 8;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              x[e] = (cv[cb] && v0 + e < V)
+                         ? a[cb] * fast_exp2(fmaf(acc[rb][cb][g * 4 + e], kLog2e, -l2[cb]))
+                         : 0.f;
+            const u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+            *(LDS_AS u32x2 *)(stg + cl * PITCH + r * 32 + g * 8 + (lane >> 5) * 4) = pk;
+          }
+        }
+      }
+      const int vp = m0 + p * RP * 32;  // first vocabulary row of the pass
+      // dz: token runs
+#pragma unroll
+      for (int it = 0; it < TOK * QPR / 64; ++it) {
+        const int q = it * 64 + lane, cl = q / QPR, pc = q - cl * QPR;
+        const int c = n0 + cl, v = vp + pc * 8;
+        const u32x4 val = *(const LDS_AS u32x4 *)(stg + cl * PITCH + pc * 8);
+        if (c < rows && v < V_pad)
+          *(u32x4 *)((unsigned short *)dz + (long long)(v >> 8) * ts + c * 256 + (v & 255)) = val;
+      }
+      // dzT: row runs of 64 tokens (n0 and the wave's 64 tokens lie in one 256-token block)
+      const int c0 = n0;
+#pragma unroll
+      for (int it = 0; it < RP * 32 * TG / 64; ++it) {
+        const int q = it * 64 + lane, r = q / TG, tg = q - r * TG;
+        const int v = vp + r;
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = (unsigned)stg[(tg * 8 + 2 * e) * PITCH + r] |
+                 ((unsigned)stg[(tg * 8 + 2 * e + 1) * PITCH + r] << 16);
+        const int c = c0 + tg * 8;
+        if (v < V_pad)
+          __builtin_nontemporal_store(
+              o, (u32x4 *)(dzt + (long long)(c >> 8) * tst + (long long)v * 256 + (c & 255)));
+      }
     }
   }
 };
