@@ -1754,27 +1754,73 @@ hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStr
 }
 
 // dz[r][idx[r][k]] -= s[r] * (sum of p over the row's entries with that index).
-// One wave per row.  Lane k compares its index with every entry of the row (64 at a
-// time through shuffles): the first entry of each distinct index sums the
-// probabilities of its later duplicates in order and does the update, so no two
-// threads touch the same element.
+// One wave per row.  The row's indices first go into a per-wave hash table in LDS: when
+// none repeats (the usual case), every entry updates its own element.  Otherwise lane k
+// compares its index with every entry of the row (64 at a time through shuffles): the
+// first entry of each distinct index sums the probabilities of its later duplicates in
+// order and does the update, so no two threads touch the same element.
+constexpr int kScatTab = 512;  // hash slots per wave (rows of up to 256 entries use it)
+
+template <int DT>
+__device__ __forceinline__ void scatter_one(void *dz, long long ts, unsigned short *dzt,
+                                            long long tst, int r, int v, float delta) {
+  if (DT == 1) {
+    unsigned short *q = (unsigned short *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
+    const unsigned short nv = f32_to_bf16(bf16_to_f32(*q) - delta);
+    *q = nv;
+    dzt[(long long)(r >> 8) * tst + (long long)v * 256 + (r & 255)] = nv;
+  } else {
+    float *q = (float *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
+    *q = *q - delta;
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigned short *dzt,
                                                  long long tst, const int32_t *idx,
                                                  const float *p, const float *srow, int rows,
                                                  int K) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  __shared__ int tab[4][kScatTab];
+  const int w = threadIdx.x >> 6;
+  const int r = blockIdx.x * 4 + w, lane = threadIdx.x & 63;
   if (r >= rows) return;
   const float sr = srow[r];
   if (sr == 0.f) return;
   const int32_t *ir = idx + (long long)r * K;
   const float *pr = p + (long long)r * K;
+  // repeated index test (a negative index lies outside this vocabulary shard: skipped)
+  bool dup = K > kScatTab / 2;
+  if (!dup) {
+    for (int i = lane; i < kScatTab; i += 64) tab[w][i] = -1;
+    for (int k = lane; k < K; k += 64) {
+      const int v = ir[k];
+      if (v < 0) continue;
+      unsigned hs = ((unsigned)v * 2654435761u) >> 23;  // 9 bits
+      for (int probe = 0; probe < kScatTab; ++probe) {  // a free slot always exists
+        const int old = atomicCAS(&tab[w][hs], -1, v);
+        if (old == -1) break;
+        if (old == v) {
+          dup = true;
+          break;
+        }
+        hs = (hs + 1) & (kScatTab - 1);
+      }
+    }
+    dup = __ballot(dup) != 0;
+  }
+  if (!dup) {
+    for (int k = lane; k < K; k += 64) {
+      const int v = ir[k];
+      if (v >= 0) scatter_one<DT>(dz, ts, dzt, tst, r, v, sr * pr[k]);
+    }
+    return;
+  }
   for (int k0 = 0; k0 < K; k0 += 64) {
     const int k = k0 + lane;
     const bool has = k < K;
     const int v = has ? ir[k] : -1;
     float tot = has ? pr[k] : 0.f;
-    bool first = has && v >= 0;  // a negative index lies outside this vocabulary shard
+    bool first = has && v >= 0;
     for (int j0 = 0; j0 < K; j0 += 64) {
       const int jl = j0 + lane;
       const int vjl = jl < K ? ir[jl] : -1;
@@ -1790,16 +1836,7 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigne
         }
       }
     }
-    if (!first) continue;
-    if (DT == 1) {
-      unsigned short *q = (unsigned short *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
-      const unsigned short nv = f32_to_bf16(bf16_to_f32(*q) - sr * tot);
-      *q = nv;
-      dzt[(long long)(r >> 8) * tst + (long long)v * 256 + (r & 255)] = nv;
-    } else {
-      float *q = (float *)dz + (long long)(v >> 8) * ts + r * 256 + (v & 255);
-      *q = *q - sr * tot;
-    }
+    if (first) scatter_one<DT>(dz, ts, dzt, tst, r, v, sr * tot);
   }
 }
 
