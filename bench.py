@@ -56,6 +56,9 @@ def parse():
                     help="measure peak device memory of one call for N = 4K .. 256K tokens "
                          "(d=3072, V=128256, K=100, chunk 4096) and fit a + b*N; prints one "
                          "JSON line and exits")
+    ap.add_argument("--dw-group-tokens", type=int, default=None,
+                    help="allocate the workspace for dW groups of at most this many tokens "
+                         "(0 = one chunk, the smallest workspace); default 16384")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="after the run, launch one plain device copy of this many GiB "
                          "(a kernel of known traffic, for scaling HBM byte counters)")
@@ -252,13 +255,14 @@ def torch_baselines():
                                           "rows": results}}), flush=True)
 
 
-def memory_sweep():
+def memory_sweep(dw_group_tokens=None):
     """Peak device memory of one fused call (inputs, outputs, workspace) against N.
 
     Inputs are generated directly in their storage types, so the peak holds only h, W,
     idx, p, mask, the outputs and the workspace.  The device's free-memory drop across
     the call is compared with the growth of torch's reserved pool: equal values show
-    the library allocated nothing of its own."""
+    the library allocated nothing of its own.  ``dw_group_tokens`` sizes the workspace
+    (None: the default 16384-token dW group; 0: one chunk)."""
     import torch
 
     import output_head_kl_amd as kd
@@ -278,11 +282,11 @@ def memory_sweep():
         p = torch.rand(N, K, device="cuda", generator=g)
         p.mul_(1.0 / K)
         mask = torch.ones(N, dtype=torch.uint8, device="cuda")
-        ws_bytes = kd.workspace_bytes(N, d, V, K, chunk)
+        ws_bytes = kd.workspace_bytes(N, d, V, K, chunk, dw_group_tokens=dw_group_tokens)
         torch.cuda.synchronize()
         free0, _ = torch.cuda.mem_get_info()
         res0 = torch.cuda.memory_reserved()
-        out = kd.fwd_bwd(h, W, idx, p, mask, chunk=chunk)
+        out = kd.fwd_bwd(h, W, idx, p, mask, chunk=chunk, dw_group_tokens=dw_group_tokens)
         torch.cuda.synchronize()
         free1, _ = torch.cuda.mem_get_info()
         res1 = torch.cuda.memory_reserved()
@@ -313,6 +317,7 @@ def memory_sweep():
     a, b, r2, resid = linfit(x[full], y[full])
     a2, b2, r22, resid2 = linfit(x, y - ws)
     res = {"memory_sweep": {"d": d, "V": V, "K": K, "chunk": chunk, "dtype": "bf16",
+                            "dw_group_tokens": 16384 if dw_group_tokens is None else dw_group_tokens,
                             "W_bytes": V * d * 2, "allocated_before_sweep_bytes": base,
                             "fit_from_N": int(x[full].min()),
                             "fit_intercept_bytes": a, "fit_bytes_per_token": b, "r2": r2,
@@ -438,7 +443,7 @@ def bench_shard(args, kd, torch, cfg, h, W, idx, p, mask):
 def main():
     args = parse()
     if args.memory_sweep:
-        memory_sweep()
+        memory_sweep(args.dw_group_tokens)
         return
     if args.torch_baselines:
         torch_baselines()
@@ -474,7 +479,8 @@ def main():
     p = torch.from_numpy(inp.p).to(dev)
     mask = torch.from_numpy(inp.mask).to(dev)
     dt_code = kd.KD_BF16 if cfg.dtype == "bf16" else kd.KD_F32
-    ws = torch.empty(kd.workspace_bytes(cfg.N, cfg.d, cfg.V, cfg.K, cfg.chunk, dt_code),
+    ws = torch.empty(kd.workspace_bytes(cfg.N, cfg.d, cfg.V, cfg.K, cfg.chunk, dt_code,
+                                        args.dw_group_tokens),
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
@@ -530,6 +536,8 @@ def main():
     tflops_recompute_equiv = 8.0 * cfg.N * cfg.V * cfg.d / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     workload = f"fused_kl_fwd_bwd_N{cfg.N}_d{cfg.d}_V{cfg.V}_K{cfg.K}_chunk{cfg.chunk}_{cfg.dtype}"
+    if args.dw_group_tokens is not None:
+        workload += f"_dwgroup{args.dw_group_tokens}"
 
     roofline = None
     kernels = {}
@@ -563,7 +571,9 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": workload, "N": cfg.N, "d": cfg.d, "V": cfg.V, "K": cfg.K,
-                   "chunk": cfg.chunk, "mask": cfg.mask},
+                   "chunk": cfg.chunk, "mask": cfg.mask,
+                   "dw_group_tokens": 16384 if args.dw_group_tokens is None else args.dw_group_tokens},
+        "workspace_bytes": ws.numel(),
         "tflops_executed_6NVd": round(tflops, 1),
         "frac_of_peak_executed": round(tflops / peak, 4),
         "tflops_recompute_equiv_8NVd": round(tflops_recompute_equiv, 1),

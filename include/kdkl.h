@@ -54,20 +54,42 @@ typedef enum {
   KD_E_ARG = 1,          /* null pointer, bad size or alignment; nothing enqueued     */
   KD_E_INDEX = 2,        /* a teacher index outside [0,V), or a probability that is
                             negative, NaN or infinite; no output written             */
-  KD_E_WORKSPACE = 3,    /* workspace smaller than kd_workspace_bytes(); nothing done */
+  KD_E_WORKSPACE = 3,    /* workspace smaller than kd_workspace_bytes_group(.., 0, ..);
+                            nothing done */
   KD_E_UNSUPPORTED = 4,  /* valid but unsupported shape (d not a multiple of 8, ...)  */
   KD_E_HIP = 5           /* a HIP runtime call failed; outputs undefined              */
 } kd_status;
 
 /*
- * kd_workspace_bytes -- device workspace needed by kd_chunked_kl_fwd_bwd.
+ * kd_workspace_bytes -- device workspace for kd_chunked_kl_fwd_bwd at full speed.
  *
  * Same size arguments as the main call.  Writes the byte count to *bytes_out.
  * Pure host computation (no GPU use).  Returns KD_OK, KD_E_ARG or
  * KD_E_UNSUPPORTED under the same rules as kd_chunked_kl_fwd_bwd.
+ * Equal to kd_workspace_bytes_group with dw_group_tokens = 16384.
  */
 int kd_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
                        int32_t dtype, size_t *bytes_out);
+
+/*
+ * kd_workspace_bytes_group -- device workspace when the dW accumulation runs over
+ * groups of at most dw_group_tokens tokens.
+ *
+ * In bfloat16, dL/dW is accumulated in float32 by one GEMM per group of chunks, and
+ * each such GEMM reads and writes the whole of dW.  The workspace holds a
+ * token-contiguous copy of the group's bf16 dz and h: (V + d) * 2 bytes per token of
+ * the group (V rounded up to 768).  The group is min(dw_group_tokens, 16384) rounded
+ * down to whole chunks, at least one chunk and at most the batch; float32 always uses
+ * one chunk.  dw_group_tokens = 0 gives the smallest workspace the calls accept: then no
+ * buffer holds more than one chunk's logits.
+ * The computing calls (kd_chunked_kl_fwd_bwd, _fwd, _bwd, kd_vocab_shard_fwd, _bwd)
+ * take the largest group, up to 16384 tokens, that the workspace passed to them
+ * holds, so the caller trades memory for speed by the size it passes; results then
+ * differ from the full-size schedule only in float rounding order.
+ * Returns KD_E_ARG for a negative dw_group_tokens, otherwise as kd_workspace_bytes.
+ */
+int kd_workspace_bytes_group(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                             int32_t dtype, int64_t dw_group_tokens, size_t *bytes_out);
 
 /*
  * kd_chunked_kl_fwd_bwd -- loss, dL/dh and dL/dW in one call.
@@ -84,7 +106,8 @@ int kd_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk
  *   row_loss  [N]     float32         optional: mask[n] ? l[n] : 0     (NULL = skip)
  *   row_lse   [N]     float32         optional: lse[n]                 (NULL = skip)
  *   zg        [N, K]  float32         optional: z[n, idx[n,k]]         (NULL = skip)
- *   workspace         >= kd_workspace_bytes(...) bytes, 256-byte aligned
+ *   workspace         256-byte aligned; kd_workspace_bytes(...) bytes for full speed,
+ *                     at least kd_workspace_bytes_group(..., 0, ...) bytes
  * Sizes: N >= 0, 1 <= K <= 32768, V >= 1, d >= 8 with d % 8 == 0, chunk >= 1,
  *   d <= 2^20, V <= 2^24, N*d and N*K below 2^62.  N == 0 writes loss = 0 and dW = 0.
  * chunk is the number of token rows whose logits are live at once; the last
@@ -118,8 +141,10 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype,
  * of kd_chunked_kl_fwd_bwd (bit for bit, on the same inputs and chunk) and writes
  *   row_lse   [N]     float32   lse[n] = log sum_v exp z[n,v]   (required when N > 0)
  * which is the state kd_chunked_kl_bwd reads.  row_loss and zg are optional (NULL =
- * skip).  dh and dW are not computed.  Same sizes, workspace (kd_workspace_bytes),
- * stream behaviour and errors as kd_chunked_kl_fwd_bwd; N == 0 writes loss = 0.
+ * skip).  dh and dW are not computed.  Same sizes, workspace, stream behaviour and
+ * errors as kd_chunked_kl_fwd_bwd; it never uses a dW group, so
+ * kd_workspace_bytes_group(..., 0, ...) bytes run it at full speed.  N == 0 writes
+ * loss = 0.
  */
 int kd_chunked_kl_fwd(const void *h, const void *W, int32_t dtype,
                       const int32_t *topk_idx, const float *topk_p,

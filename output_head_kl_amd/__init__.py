@@ -46,6 +46,9 @@ def _lib():
     i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
     lib.kd_workspace_bytes.argtypes = [i64, i64, i64, i32, i64, i32, ctypes.POINTER(sz)]
     lib.kd_workspace_bytes.restype = ctypes.c_int
+    lib.kd_workspace_bytes_group.argtypes = [i64, i64, i64, i32, i64, i32, i64,
+                                             ctypes.POINTER(sz)]
+    lib.kd_workspace_bytes_group.restype = ctypes.c_int
     lib.kd_chunked_kl_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
                                           vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_fwd_bwd.restype = ctypes.c_int
@@ -88,9 +91,16 @@ def _check(rc: int) -> None:
         raise KDError(rc, _lib().kd_last_error().decode())
 
 
-def workspace_bytes(N: int, d: int, V: int, K: int, chunk: int, dtype: int = KD_BF16) -> int:
+def workspace_bytes(N: int, d: int, V: int, K: int, chunk: int, dtype: int = KD_BF16,
+                    dw_group_tokens: Optional[int] = None) -> int:
+    """Workspace bytes: for the default dW group (``dw_group_tokens=None``) or for groups
+    of at most ``dw_group_tokens`` tokens (0 = one chunk, the smallest accepted)."""
     out = ctypes.c_size_t(0)
-    _check(_lib().kd_workspace_bytes(N, d, V, K, chunk, dtype, ctypes.byref(out)))
+    if dw_group_tokens is None:
+        _check(_lib().kd_workspace_bytes(N, d, V, K, chunk, dtype, ctypes.byref(out)))
+    else:
+        _check(_lib().kd_workspace_bytes_group(N, d, V, K, chunk, dtype, dw_group_tokens,
+                                               ctypes.byref(out)))
     return int(out.value)
 
 
@@ -132,10 +142,10 @@ def _prep(h, W, topk_idx, topk_p, loss_mask):
     return dt, N, d, V, K, loss_mask
 
 
-def _workspace(workspace, N, d, V, K, chunk, dt, dev):
+def _workspace(workspace, N, d, V, K, chunk, dt, dev, dw_group_tokens=None):
     import torch
     if workspace is None:
-        workspace = torch.empty(max(workspace_bytes(N, d, V, K, chunk, dt), 256),
+        workspace = torch.empty(max(workspace_bytes(N, d, V, K, chunk, dt, dw_group_tokens), 256),
                                 dtype=torch.uint8, device=dev)
     return workspace
 
@@ -146,7 +156,7 @@ def _stream(stream, dev):
 
 
 def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: bool = False,
-            workspace=None, stream=None):
+            workspace=None, stream=None, dw_group_tokens: Optional[int] = None):
     """Mean top-K KL loss with its gradients, computed chunk by chunk on the GPU.
 
     Args (torch CUDA tensors, contiguous):
@@ -154,14 +164,16 @@ def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: boo
       topk_idx [N, K] int32; topk_p [N, K] float32; loss_mask [N] uint8/bool or None.
       chunk: token rows whose logits are live at once.
       rows: also return per-row loss, logsumexp and the logits at the teacher's indices.
-      workspace: optional uint8 tensor of at least ``workspace_bytes(...)`` bytes.
+      workspace: optional uint8 tensor; the call takes the largest dW group it holds.
+      dw_group_tokens: size of the workspace allocated when none is given (see
+        ``workspace_bytes``); None is the default, full-speed group.
     Returns (loss[1] f32, dh [N, d] dtype, dW [V, d] f32) and, with ``rows``,
     (row_loss [N], row_lse [N], zg [N, K]) as float32.
     """
     import torch
     dt, N, d, V, K, loss_mask = _prep(h, W, topk_idx, topk_p, loss_mask)
     dev = h.device
-    workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev)
+    workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev, dw_group_tokens)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     dh = torch.empty((N, d), dtype=h.dtype, device=dev)
     dW = torch.empty((V, d), dtype=torch.float32, device=dev)
@@ -186,7 +198,7 @@ def fwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: bool = 
     import torch
     dt, N, d, V, K, loss_mask = _prep(h, W, topk_idx, topk_p, loss_mask)
     dev = h.device
-    workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev)
+    workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev, 0)  # no dW group
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     row_lse = torch.empty(N, dtype=torch.float32, device=dev)
     row_loss = zg = None
@@ -203,10 +215,11 @@ def fwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: bool = 
 
 
 def bwd(h, W, topk_idx, topk_p, row_lse, grad_loss=None, loss_mask=None, chunk: int = 2048,
-        workspace=None, stream=None):
+        workspace=None, stream=None, dw_group_tokens: Optional[int] = None):
     """Backward half: (dh [N, d] dtype, dW [V, d] f32) for the upstream gradient
     ``grad_loss`` (a one-element float32 CUDA tensor; None means 1), recomputing the
-    logits from h and W with the ``row_lse`` saved by ``fwd``."""
+    logits from h and W with the ``row_lse`` saved by ``fwd``.  ``workspace`` and
+    ``dw_group_tokens`` as in ``fwd_bwd``."""
     import torch
     dt, N, d, V, K, loss_mask = _prep(h, W, topk_idx, topk_p, loss_mask)
     dev = h.device
@@ -218,7 +231,7 @@ def bwd(h, W, topk_idx, topk_p, row_lse, grad_loss=None, loss_mask=None, chunk: 
     if grad_loss.dtype != torch.float32:
         raise TypeError("grad_loss must be float32")
     grad_loss = grad_loss.contiguous()
-    workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev)
+    workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev, dw_group_tokens)
     dh = torch.empty((N, d), dtype=h.dtype, device=dev)
     dW = torch.empty((V, d), dtype=torch.float32, device=dev)
     _check(_lib().kd_chunked_kl_bwd(
@@ -292,7 +305,7 @@ def vocab_shard_fwd(h, W_shard, topk_idx, topk_p, v_offset: int, V_total: int,
     import torch
     dt, N, d, Vs, K, _ = _prep(h, W_shard, topk_idx, topk_p, None)
     dev = h.device
-    workspace = _workspace(workspace, N, d, Vs, K, chunk, dt, dev)
+    workspace = _workspace(workspace, N, d, Vs, K, chunk, dt, dev, 0)  # no dW group
     st = [torch.empty(N, dtype=torch.float32, device=dev) for _ in range(3)]
     zgt = torch.empty((N, K), dtype=torch.float32, device=dev) if zg else None
     _check(_lib().kd_vocab_shard_fwd(

@@ -98,7 +98,7 @@ void prof_end(int cls, hipStream_t s) {
 }
 
 bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
-                 Layout *L) {
+                 int64_t dw_group_tokens, Layout *L) {
   const int64_t es = dtype == KD_BF16 ? 2 : 4;
   const int64_t Nn = N > 0 ? N : 1;
   L->C = chunk < Nn ? chunk : Nn;
@@ -143,8 +143,9 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->off_idxloc = take((size_t)L->C_alloc * K * 4);
   {
     const int64_t nchunks = (Nn + L->C - 1) / L->C;
-    int64_t g = dtype == KD_BF16 && L->C_alloc < kDwGroupTokens ? kDwGroupTokens / L->C_alloc : 1;
-    L->dw_group = (int)(g < nchunks ? g : nchunks);
+    int64_t g = dtype == KD_BF16 ? dw_group_tokens / L->C_alloc : 1;
+    if (g > nchunks) g = nchunks;
+    L->dw_group = (int)(g < 1 ? 1 : g);
   }
   L->off_dzt = take(dtype == KD_BF16 ? (size_t)L->V_pad * L->dw_group * L->C_alloc * 2 : 0);
   L->off_ht = take(dtype == KD_BF16 ? (size_t)d * L->dw_group * L->C_alloc * 2 : 0);
@@ -160,16 +161,23 @@ int kd_version(void) { return 2; }
 
 const char *kd_last_error(void) { return g_err; }
 
-int kd_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_t dtype,
-                       size_t *bytes_out) {
+int kd_workspace_bytes_group(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                             int32_t dtype, int64_t dw_group_tokens, size_t *bytes_out) {
   g_err[0] = 0;
   if (!bytes_out) return fail(KD_E_ARG, "bytes_out is NULL");
   int rc = check_sizes(N, d, V, K, chunk, dtype);
   if (rc != KD_OK) return rc;
+  if (dw_group_tokens < 0) return fail(KD_E_ARG, "dw_group_tokens is negative");
+  if (dw_group_tokens > kd::kDwGroupTokens) dw_group_tokens = kd::kDwGroupTokens;
   kd::Layout L;
-  kd::make_layout(N, d, V, K, chunk, dtype, &L);
+  kd::make_layout(N, d, V, K, chunk, dtype, dw_group_tokens, &L);
   *bytes_out = L.total;
   return KD_OK;
+}
+
+int kd_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_t dtype,
+                       size_t *bytes_out) {
+  return kd_workspace_bytes_group(N, d, V, K, chunk, dtype, kd::kDwGroupTokens, bytes_out);
 }
 
 }  // extern "C"
@@ -227,10 +235,14 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
       mis(row_lse, 4) || mis(zg, 4) || mis(lse_in, 4) || mis(grad_loss, 4))
     return fail(KD_E_ARG, "index, probability and float arguments must be 4-byte aligned");
   if (mis(workspace, 256)) return fail(KD_E_ARG, "workspace must be 256-byte aligned");
+  // The dW group is the largest (up to kDwGroupTokens tokens) whose copies fit.
   kd::Layout L;
-  kd::make_layout(N, d, V, K, chunk, dtype, &L);
+  kd::make_layout(N, d, V, K, chunk, dtype, kd::kDwGroupTokens, &L);
+  while (workspace_bytes < L.total && L.dw_group > 1)
+    kd::make_layout(N, d, V, K, chunk, dtype, (int64_t)(L.dw_group - 1) * L.C_alloc, &L);
   if (workspace_bytes < L.total)
-    return fail(KD_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    return fail(KD_E_WORKSPACE, "workspace has %zu bytes, needs at least %zu", workspace_bytes,
+                L.total);
 
   hipStream_t stream = (hipStream_t)stream_v;
   char *ws = (char *)workspace;

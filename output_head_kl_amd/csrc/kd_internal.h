@@ -18,7 +18,8 @@ constexpr int kTileA16 = 384;
 inline int tile_rows(int dtype) { return dtype == 1 ? kTileA16 : kTile; }
 // Tokens per dW GEMM launch (bf16): each launch adds its product into the fp32 dW, a
 // read and a write of all of dW, so chunks are grouped up to this many tokens (and never
-// more chunks than the batch has).
+// more chunks than the batch has).  This is the default; a call whose workspace is
+// smaller takes the largest group it holds, down to one chunk.
 constexpr int kDwGroupTokens = 16384;
 
 // Kernel classes for timing (kd_profile_*).
@@ -51,14 +52,15 @@ struct Layout {
   int64_t k_split;    // vocabulary rows per split (a multiple of 256)
   int64_t nkeys;      // buckets per chunk: V_pad / tv * C_alloc / 256
   int dw_group;       // chunks per dW GEMM (bf16): dzT and hT hold dw_group chunks side by
-                      // side, so fp32 dW is read and written once per ~kDwGroupTokens tokens
+                      // side, so fp32 dW is read and written once per dw_group chunks
   size_t off_flags, off_acc, off_partials, off_lse, off_sM, off_s, off_rowterm, off_zg,
       off_dz, off_dhpart, off_bcount, off_bcursor, off_boff, off_bent, off_wt, off_idxloc,
       off_dzt, off_ht, total;
 };
 
+// dw_group_tokens caps the dW group (whole chunks, at least one; fp32 always uses one).
 bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
-                 Layout *L);
+                 int64_t dw_group_tokens, Layout *L);
 
 // --- launchers (all asynchronous on `s`; return hipSuccess or the launch error) ---
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);

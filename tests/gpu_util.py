@@ -52,18 +52,19 @@ def to_f64(t, torch):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def run_raw(inp: synth.Inputs, torch, chunk=None, rows=True, use_mask=True):
-    """Outputs of the HIP path as torch tensors on the device."""
+def run_raw(inp: synth.Inputs, torch, chunk=None, rows=True, use_mask=True, **kw):
+    """Outputs of the HIP path as torch tensors on the device (``kw`` goes to fwd_bwd)."""
     import output_head_kl_amd as kd
     h, W, idx, p, mask = to_device(inp, torch)
     out = kd.fwd_bwd(h, W, idx, p, mask if use_mask else None,
-                     chunk=chunk or inp.cfg.chunk, rows=rows)
+                     chunk=chunk or inp.cfg.chunk, rows=rows, **kw)
     torch.cuda.synchronize()
     del h, W, idx, p, mask
     names = ["loss", "dh", "dW", "row_loss", "row_lse", "zg"][:len(out)]
     return dict(zip(names, out))
 
 
-def run(inp: synth.Inputs, torch, chunk=None, rows=True, use_mask=True):
+def run(inp: synth.Inputs, torch, chunk=None, rows=True, use_mask=True, **kw):
     """Outputs of the HIP path as float64 numpy arrays."""
-    return {k: to_f64(v, torch) for k, v in run_raw(inp, torch, chunk, rows, use_mask).items()}
+    return {k: to_f64(v, torch)
+            for k, v in run_raw(inp, torch, chunk, rows, use_mask, **kw).items()}

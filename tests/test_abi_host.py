@@ -63,6 +63,28 @@ def test_workspace_is_bounded_and_constant_beyond_one_dw_group(lib):
     assert sizes == sorted(sizes)
 
 
+def test_workspace_for_a_smaller_dw_group(lib):
+    """Each token of the dW group costs (V_pad + d) * 2 bytes; group 0 (one chunk) keeps
+    no more than one chunk's logits anywhere, and 16384 is the default."""
+    args = (32768, 3072, 128256, 100, 2048)
+    full = kd.workspace_bytes(*args)
+    assert kd.workspace_bytes(*args, dw_group_tokens=16384) == full
+    assert kd.workspace_bytes(*args, dw_group_tokens=1 << 30) == full
+    one = kd.workspace_bytes(*args, dw_group_tokens=0)
+    assert kd.workspace_bytes(*args, dw_group_tokens=2047) == one
+    assert kd.workspace_bytes(*args, dw_group_tokens=2048) == one
+    per_token = (128256 + 3072) * 2
+    for g in (2, 3, 5, 8):
+        assert kd.workspace_bytes(*args, dw_group_tokens=g * 2048 + 100) == one + (g - 1) * 2048 * per_token
+    assert full == one + 7 * 2048 * per_token
+    dz, wt = 2048 * 128256 * 2, 128256 * 3072 * 2
+    assert 2 * dz + wt < one < 2 * dz + wt + 600_000_000
+    # fp32 always accumulates dW chunk by chunk
+    assert kd.workspace_bytes(*args, kd.KD_F32, 0) == kd.workspace_bytes(*args, kd.KD_F32)
+    out = ctypes.c_size_t(0)
+    assert lib.kd_workspace_bytes_group(*args, 1, -1, ctypes.byref(out)) == E_ARG
+
+
 @pytest.mark.parametrize("args,code", [
     ((10, 12, 100, 4, 8, 1), E_UNSUPPORTED),     # d not a multiple of 8
     ((10, 16, 100, 0, 8, 1), E_ARG),             # K = 0
@@ -113,7 +135,9 @@ def test_entry_point_rejects_bad_calls_on_host(lib, kw, code):
 
 
 def test_workspace_too_small_reports_needed_size(lib):
-    need = kd.workspace_bytes(64, 64, 1000, 4, 32)
+    """Below the one-chunk dW group the call fails; the message gives that size."""
+    need = kd.workspace_bytes(64, 64, 1000, 4, 32, dw_group_tokens=0)
+    assert need < kd.workspace_bytes(64, 64, 1000, 4, 32)
     assert _call(lib, wsb=need - 1) == E_WORKSPACE
     assert str(need).encode() in lib.kd_last_error()
 

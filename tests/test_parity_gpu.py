@@ -1,10 +1,12 @@
 """HIP path against the CPU oracle, element by element, on the same seeded inputs.
 
 Small and ragged shapes are compared in full (several tiles, a partial last chunk,
-V and d off the tile grid).  The full-size workloads are compared on 512 sampled token
-rows (per-row loss, logsumexp, gathered logits and dh rows, with the batch's own
-count) plus the whole dW of a 512-row sub-batch run through the same kernels, and the
-mean loss is checked against the per-row losses the GPU returns.
+V and d off the tile grid), and so are the 4096- and 32768-token workloads at
+d=3072, V=128256, K=100 (loss, dh, dW and every row's loss, logsumexp and gathered
+logits).  Every full-size workload, the 262144-token one included, is also compared on
+512 sampled token rows (per-row loss, logsumexp, gathered logits and dh rows, with the
+batch's own count) plus the whole dW of a 512-row sub-batch run through the same
+kernels, and its mean loss is checked against the per-row losses the GPU returns.
 """
 import numpy as np
 import pytest
@@ -168,6 +170,41 @@ def test_gradient_invariants_on_gpu(torch_cuda):
     assert abs(a - b) <= 1e-4 * max(abs(a), abs(b))
 
 
+@pytest.mark.parametrize("group", [0, 1100, 1600])
+def test_smaller_dw_group_workspace(torch_cuda, group):
+    """A workspace sized for a smaller dW group (one, two or three 300-token chunks of
+    five, so the last group is partial) gives the fused call's loss, row outputs and dh
+    bit for bit, and dW within the tolerance; the backward half likewise."""
+    torch = torch_cuda
+    import output_head_kl_amd as kd
+    inp = synth.make(1, seed=31, N=1500, d=136, V=3001, K=7, chunk=300, dtype="bf16")
+    inp.mask[[3, 700, 1499]] = 0
+    base = run(inp, torch)
+    got = run(inp, torch, dw_group_tokens=group)
+    for k in ("loss", "dh", "row_loss", "row_lse", "zg"):
+        assert np.array_equal(got[k], base[k]), k
+    ref = _check_full(inp, got)
+    assert rel_fro(got["dW"], base["dW"]) < 1e-5
+    h, W, idx, p, mask = to_device(inp, torch)
+    lse = torch.from_numpy(ref["row_lse"].astype(np.float32)).cuda()
+    dh_a, dW_a = kd.bwd(h, W, idx, p, lse, None, mask, chunk=300)
+    dh_b, dW_b = kd.bwd(h, W, idx, p, lse, None, mask, chunk=300, dw_group_tokens=group)
+    assert bool(torch.equal(dh_a, dh_b))
+    assert rel_fro(to_f64(dW_b, torch), ref["dW"]) <= TOL["bf16"]["grad"]
+    assert rel_fro(to_f64(dW_b, torch), to_f64(dW_a, torch)) < 1e-5
+
+
+def test_workspace_below_one_chunk_group_is_rejected(torch_cuda):
+    torch = torch_cuda
+    import output_head_kl_amd as kd
+    inp = synth.make(1, seed=32, N=600, d=64, V=1000, K=4, chunk=200, dtype="bf16")
+    h, W, idx, p, mask = to_device(inp, torch)
+    need = kd.workspace_bytes(600, 64, 1000, 4, 200, dw_group_tokens=0)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kd.KDError, match="KD_E_WORKSPACE"):
+        kd.fwd_bwd(h, W, idx, p, mask, chunk=200, workspace=ws)
+
+
 # ------------------------------------------------------------------ full-size workloads
 _CACHE = {}
 
@@ -220,3 +257,74 @@ def test_full_size_workload_on_sampled_rows(torch_cuda, cid):
     assert errs["loss"] <= tol["loss"], errs
     assert errs["dW"] <= tol["grad"], errs
     assert errs["dh"] <= tol["grad"], errs
+
+
+# ------------------------------------------------- the 4K- and 32K-token workloads in full
+# Rows are independent, so the oracle's batch is taken in equal row parts: a part's own
+# call weighs its rows by 1/count_part, and multiplying its dh rows, dW and summed loss by
+# count_part/count gives that part's exact share of the whole batch's mean.  Each part is a
+# test of its own (about half a minute of host time each) and checks its rows; the last
+# part adds up every part's dW and loss and checks the batch's totals.
+_PARTS = {1: 1, 2: 4}
+_STATE = {}
+
+
+def _state(torch, cid):
+    st = _STATE.get(cid)
+    if st is None:
+        _STATE.clear()
+        inp = synth.make(cid)
+        got = run(inp, torch, rows=True)
+        st = dict(inp=inp, got=got, h64=inp.h64(), W64=inp.W64(),
+                  count=int((inp.mask != 0).sum()), parts={})
+        _STATE[cid] = st
+    return st
+
+
+def _part(st, cid, q):
+    if q not in st["parts"]:
+        inp, n = st["inp"], st["inp"].cfg.N // _PARTS[cid]
+        r0, r1 = q * n, (q + 1) * n if q + 1 < _PARTS[cid] else inp.cfg.N
+        ref = oracle.forward_backward(st["h64"][r0:r1], st["W64"], inp.idx[r0:r1],
+                                      inp.p[r0:r1], inp.mask[r0:r1], block_rows=128)
+        w = ref["count"] / st["count"]
+        st["parts"][q] = dict(r0=r0, r1=r1, dh=ref["dh"] * w, dW=ref["dW"] * w,
+                              loss_sum=ref["loss"] * ref["count"], row_loss=ref["row_loss"],
+                              row_lse=ref["row_lse"], zg=ref["zg"])
+    return st["parts"][q]
+
+
+@pytest.mark.parametrize("cid,part", [(1, 0)] + [(2, q) for q in range(_PARTS[2])])
+def test_workload_in_full(torch_cuda, cid, part):
+    st = _state(torch_cuda, cid)
+    cfg, got, tol = st["inp"].cfg, st["got"], TOL[st["inp"].cfg.dtype]
+    ref = _part(st, cid, part)
+    r0, r1 = ref["r0"], ref["r1"]
+    errs = dict(row_loss=rel_fro(got["row_loss"][r0:r1], ref["row_loss"]),
+                row_lse=max_abs_rel(got["row_lse"][r0:r1], ref["row_lse"]),
+                zg=rel_fro(got["zg"][r0:r1], ref["zg"]),
+                dh=rel_fro(got["dh"][r0:r1], ref["dh"]))
+    print(f"config {cid} {cfg.name} rows {r0}..{r1}:", {k: f"{v:.2e}" for k, v in errs.items()},
+          flush=True)
+    assert errs["row_loss"] <= tol["loss"], errs
+    assert errs["row_lse"] <= tol["loss"], errs
+    assert errs["zg"] <= tol["grad"], errs
+    assert errs["dh"] <= tol["grad"], errs
+    masked = st["inp"].mask[r0:r1] == 0
+    assert np.all(got["dh"][r0:r1][masked] == 0.0)
+    if part + 1 < _PARTS[cid]:
+        return
+    parts = [_part(st, cid, q) for q in range(_PARTS[cid])]
+    dW = parts[0]["dW"]
+    for x in parts[1:]:
+        dW += x["dW"]
+    loss = sum(x["loss_sum"] for x in parts) / st["count"]
+    dh = np.concatenate([x["dh"] for x in parts])
+    errs = dict(loss=rel(got["loss"][0], loss), dh=rel_fro(got["dh"], dh),
+                dW=rel_fro(got["dW"], dW))
+    print(f"config {cid} {cfg.name} whole batch:", {k: f"{v:.2e}" for k, v in errs.items()},
+          flush=True)
+    _STATE.clear()
+    assert errs["loss"] <= tol["loss"], errs
+    assert errs["dh"] <= tol["grad"], errs
+    assert errs["dW"] <= tol["grad"], errs
