@@ -72,6 +72,57 @@ def test_wide_logit_range(torch_cuda, dtype):
     _check_full(inp, run(inp, torch_cuda))
 
 
+def _uniform_teacher(N, V, K, rng):
+    """K distinct uniform indices per row (a permutation when K = V) and probabilities
+    from the softmax of sorted N(0, 2) scores, scaled to a mass of 0.9."""
+    idx = np.argsort(rng.random((N, V)), axis=1)[:, :K].astype(np.int32)
+    sc = -np.sort(-rng.normal(0.0, np.sqrt(2.0), (N, K)), axis=1)
+    e = np.exp(sc - sc[:, :1])
+    return idx, (0.9 * e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype,V,K", [("bf16", 3001, 300), ("f32", 2000, 1100),
+                                       ("bf16", 700, 700)])
+def test_large_k(torch_cuda, dtype, V, K):
+    """K above the 256 indices a scatter wave hashes (so every row takes the path that
+    sums repeats first), up to K = V; some rows repeat entries, one of them many times."""
+    rng = np.random.default_rng(40 + K)
+    inp = synth.make(1, seed=41, N=300, d=72, V=V, K=4, chunk=128, dtype=dtype)
+    inp.idx, inp.p = _uniform_teacher(300, V, K, rng)
+    inp.idx[5, 1] = inp.idx[5, 0]
+    inp.idx[200, K - 1] = inp.idx[200, 3]
+    inp.idx[201, : K // 2] = inp.idx[201, K - 1]
+    inp.mask[[7, 150]] = 0
+    _check_full(inp, run(inp, torch_cuda))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_student_equal_to_teacher_gives_zero(torch_cuda, dtype):
+    """K = V with the teacher's probabilities equal to the student's softmax (from the
+    oracle's logits of the same inputs): the loss and both gradients vanish, up to
+    rounding, against the gradients of a random teacher.  In bf16 the floor is dz's own
+    rounding (2^-9 of each M*softmax entry, which the exact p no longer cancels): about
+    7e-4 of the random teacher's gradients; fp32 reaches about 3e-7."""
+    N, V = 200, 600
+    rng = np.random.default_rng(50)
+    inp = synth.make(1, seed=51, N=N, d=64, V=V, K=4, chunk=64, dtype=dtype)
+    Z = inp.h64() @ inp.W64().T
+    q = np.exp(Z - Z.max(axis=1, keepdims=True))
+    q /= q.sum(axis=1, keepdims=True)
+    inp.idx = np.argsort(rng.random((N, V)), axis=1).astype(np.int32)
+    inp.p = np.take_along_axis(q, inp.idx, axis=1).astype(np.float32)
+    got = run(inp, torch_cuda)
+    scale = run(synth.make(1, seed=51, N=N, d=64, V=V, K=8, chunk=64, dtype=dtype), torch_cuda)
+    print(dtype, "loss", got["loss"][0], "max row loss", np.abs(got["row_loss"]).max(),
+          "dh ratio", np.linalg.norm(got["dh"]) / np.linalg.norm(scale["dh"]),
+          "dW ratio", np.linalg.norm(got["dW"]) / np.linalg.norm(scale["dW"]), flush=True)
+    assert abs(got["loss"][0]) < 1e-5
+    assert np.abs(got["row_loss"]).max() < 2e-5
+    floor = 5e-3 if dtype == "bf16" else 1e-5
+    assert np.linalg.norm(got["dh"]) < floor * np.linalg.norm(scale["dh"])
+    assert np.linalg.norm(got["dW"]) < floor * np.linalg.norm(scale["dW"])
+
+
 def test_tiny_chunks_and_single_token(torch_cuda):
     inp = synth.make(0, seed=5, N=37, d=8, V=300, K=3, chunk=1, dtype="bf16")
     _check_full(inp, run(inp, torch_cuda))
