@@ -310,6 +310,30 @@ void gemm_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
   epi(acc, m0 + wr * 128, n0 + wc * 128, lane, split, smem);
 }
 
+// Accumulator number s = (rb * NCB + cb) * 16 + i of a lane.  s is wave-uniform, so the
+// switch becomes a tree of scalar branches that ends in one register move.
+template <int NRB, int NCB, int S>
+__device__ __forceinline__ float acc_at(const f32x16 (&acc)[NRB][NCB]) {
+  if constexpr (S < NRB * NCB * 16) return acc[S / (16 * NCB)][(S / 16) % NCB][S % 16];
+  else return 0.f;
+}
+template <int NRB, int NCB>
+__device__ __forceinline__ float pick_acc(const f32x16 (&acc)[NRB][NCB], int s) {
+  static_assert(NRB * NCB * 16 <= 256, "at most 256 accumulators per lane");
+  switch (s) {
+#define KD_ACC1(n) case n: return acc_at<NRB, NCB, n>(acc);
+#define KD_ACC4(n) KD_ACC1(n) KD_ACC1(n + 1) KD_ACC1(n + 2) KD_ACC1(n + 3)
+#define KD_ACC16(n) KD_ACC4(n) KD_ACC4(n + 4) KD_ACC4(n + 8) KD_ACC4(n + 12)
+#define KD_ACC64(n) KD_ACC16(n) KD_ACC16(n + 16) KD_ACC16(n + 32) KD_ACC16(n + 48)
+    KD_ACC64(0) KD_ACC64(64) KD_ACC64(128) KD_ACC64(192)
+#undef KD_ACC64
+#undef KD_ACC16
+#undef KD_ACC4
+#undef KD_ACC1
+    default: return 0.f;
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // Epilogues
 // ---------------------------------------------------------------------------------
@@ -319,13 +343,17 @@ void gemm_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
 //  * per (token, WR vocabulary rows): max and sum of exp(z - max) -> part, at index
 //    (first row of the wave) / WR;
 //  * gather: the tile's teacher hits (bucket key = vocabulary tile * token tiles + token
-//    tile, entries packed c_local | v_local << 8 | k << 17) read z from the tile, staged
-//    through LDS in slices of 64 vocabulary rows ([256 tokens][68] fp32, 68 KB);
+//    tile, entries packed c_local | v_local << 8 | k << 17) read z from the tile: up to
+//    64 hits straight from the owning lane's accumulator, more through LDS in slices of
+//    64 vocabulary rows ([256 tokens][68] fp32, 68 KB);
 //  * optionally (u != null) u = exp(z - max) itself, in dz's layout, for the single-sweep
 //    backward (launch_rescale_dz turns it into dz once the logsumexp is known).
 template <int DT>
 struct EpiFwdLse {
   static constexpr bool kPrefetch = true;
+  // Tiles with at most this many teacher hits take them straight from the accumulators
+  // (every wave holds the tile's entries, one per lane); others stage z through LDS.
+  static constexpr int kDirect = 64;
   float2 *part;   // [n_lse][ld] (max, sum exp(z - max)) per wave row of the tile
   long long ld;
   int V, rows;
@@ -338,8 +366,9 @@ struct EpiFwdLse {
   long long ts;           // C_alloc * 256
   int V_pad;
   // The tile's bucket of teacher hits: [beg, end) of the entries, and when the tile has
-  // at most one hit per thread, this thread's entry (else ~0).  The pipelined core loads
-  // it before its k-loop, so that the loads' latency hides behind the loop.
+  // at most one hit per thread, this thread's entry (else ~0); with at most kDirect hits,
+  // entry `lane` in every wave.  The pipelined core loads it before its k-loop, so that
+  // the loads' latency hides behind the loop.
   struct Pre {
     int beg, end;
     unsigned ent1;
@@ -351,10 +380,29 @@ struct EpiFwdLse {
     Pre pr;
     pr.beg = boff[key];
     pr.end = boff[key + 1];
-    const int t = threadIdx.x;
-    pr.ent1 = pr.end - pr.beg <= (int)blockDim.x && pr.beg + t < pr.end ? bent[pr.beg + t]
-                                                                          : 0xFFFFFFFFu;
+    const int n = pr.end - pr.beg;
+    const int j = n <= kDirect ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
+    pr.ent1 = n <= (int)blockDim.x && j < n ? bent[pr.beg + j] : 0xFFFFFFFFu;
     return pr;
+  }
+  // Each wave walks the tile's n entries (held one per lane) and takes those in its own
+  // rows and columns: the owning lane holds z in accumulator
+  // (rb, cb, i) for wave-local row r = 32 rb + 8 (i / 4) + 4 (lane / 32) + i % 4 and
+  // column c = 32 cb + lane % 32.
+  template <int NRB, int NCB>
+  __device__ __forceinline__ void gather_direct(const f32x16 (&acc)[NRB][NCB], int m0, int n0,
+                                                int lane, int tn, int n, unsigned ent1) const {
+    constexpr int WR = 32 * NRB, WNC = 32 * NCB;
+    const int rlo = m0 % (2 * WR), clo = n0 & 255;
+    for (int e = 0; e < n; ++e) {
+      const unsigned ent = (unsigned)__builtin_amdgcn_readlane((int)ent1, e);
+      const int cl = (int)(ent & 255), k = (int)(ent >> 17);
+      const int r = (int)((ent >> 8) & 511) - rlo, c = cl - clo;
+      if ((unsigned)r >= (unsigned)WR || (unsigned)c >= (unsigned)WNC) continue;
+      const int rr = r & 31;
+      const float v = pick_acc(acc, ((r >> 5) * NCB + (c >> 5)) * 16 + ((rr >> 3) << 2) + (rr & 3));
+      if (lane == (c & 31) + (((rr >> 2) & 1) << 5)) zg[(long long)(tn * 256 + cl) * K + k] = v;
+    }
   }
   template <int NRB, int NCB>
   __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
@@ -371,7 +419,9 @@ struct EpiFwdLse {
     // hit per thread, each thread's entry was loaded once (prefetch) for every pass.
     const int tm = m0 / TR, tn = n0 >> 8;
     const int beg = pr.beg, end = pr.end;
-    if (beg != end) {
+    if (beg != end && end - beg <= kDirect) {
+      gather_direct(acc, m0, n0, lane, tn, end - beg, pr.ent1);
+    } else if (beg != end) {
       const int t = threadIdx.x, wr = (m0 - tm * TR) / WR;
       constexpr int P = 68, SLB = 256 * P * 4;      // slice pitch (floats), slice bytes
       constexpr int NS = 2 * SPW;                   // 64-row slices in the tile
