@@ -141,8 +141,13 @@ def bench_topk(args):
         kd._check(lib.kd_teacher_topk(x.data_ptr(), kd.KD_BF16, N, V, K, idx.data_ptr(),
                                       pr.data_ptr(), lse.data_ptr(), ws.data_ptr(), 256, strm))
 
-    for _ in range(args.warmup):
+    # A call takes ~1.5 ms, so a few calls do not bring the GPU to its steady clock:
+    # warm up for at least half a second (and at least `warmup` calls)
+    t0 = time.perf_counter()
+    nw = 0
+    while nw < args.warmup or time.perf_counter() - t0 < 0.5:
         call()
+        nw += 1
     torch.cuda.synchronize()
     kd.profile_read()
     kd.profile_enable(True)

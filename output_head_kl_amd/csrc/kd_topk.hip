@@ -207,10 +207,14 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
   // order is the float order, +0.0 and -0.0 alike); -inf lets everything through.
   uint64_t tge = 0;
   float tf = -INFINITY;
-  // running max and sum of exp(x - max) per lane; the sum is kept in float64 (a row
-  // has ~V/256 terms per lane), each term is a float32 exp2.  A NaN or +inf logit
-  // makes the final sum NaN or the maximum +inf, which is how bad rows are found.
-  float m = -INFINITY;
+  // running max m and sum of exp(x - max) per lane, in base 2: with m2 = m * log2(e)
+  // rounded once, each term is exp2(x * log2(e) - m2) from one fused multiply-add, and
+  // the same m2 is the reference of every later use of the sum (the rescale when the
+  // max rises, the combine across lanes and the probabilities), so its rounding cancels.
+  // The sum is kept in float64 (a row has ~V/256 terms per lane), each term is a
+  // float32 exp2.  A NaN or +inf logit makes the final sum NaN or the maximum +inf,
+  // which is how bad rows are found.
+  float m = -INFINITY, m2 = -INFINITY;
   double s = 0.0;
   int bad = 0;
   const int nchunks = (int)((V + CHUNK - 1) / CHUNK);
@@ -253,7 +257,8 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
   for (int u = 0; u < PF; ++u) {
     const int ci = c0 + u;
     const int e0 = ci * CHUNK + t * EPL;
-    // all EPL elements of a lane are in the row or none is (V % EPL == 0 when VEC)
+    // all EPL elements of a lane are in the row or none is (V % EPL == 0 when VEC); a
+    // lane past the row (loaded zeros) is masked as a whole, never element by element
     const bool in = e0 < Vi;
     float x[EPL];
     {
@@ -264,29 +269,33 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
         if (DT == 1) b = VEC ? ((j & 1) ? (wd[j >> 1] & 0xFFFF0000u) : (wd[j >> 1] << 16))
                              : (wd[0] << 16);
         else b = VEC ? wd[j] : wd[0];
-        x[j] = in ? __uint_as_float(b) : -INFINITY;
+        x[j] = __uint_as_float(b);
       }
     }
     ring[u] = load_raw(ci + PF);
     // online logsumexp of this lane
-    float lm = x[0];
+    float lm = -INFINITY;
+    if (in) {
+      lm = x[0];
 #pragma unroll
-    for (int j = 1; j < EPL; ++j) lm = fmaxf(lm, x[j]);
-    if (lm > m) {
-      s = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f((m - lm) * kTkLog2e);
-      m = lm;
-    }
-    if (m != -INFINITY) {
-      // (x - m) first: the difference of two logits is exact or nearly so, while
-      // x * log2(e) - m * log2(e) would lose |m| * 2^-24 to the rounding of m * log2(e)
-      float part = 0.f;  // at most 8 terms in float32
+      for (int j = 1; j < EPL; ++j) lm = fmaxf(lm, x[j]);
+      if (lm > m) {
+        asm volatile("");  // rare: keep it a branch rather than computed every chunk
+        const float lm2 = lm * kTkLog2e;
+        s = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f(m2 - lm2);
+        m = lm;
+        m2 = lm2;
+      }
+      if (m != -INFINITY) {
+        float part = __builtin_amdgcn_exp2f(fmaf(x[0], kTkLog2e, -m2));  // <= 8 terms
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) part += __builtin_amdgcn_exp2f((x[j] - m) * kTkLog2e);
-      s += (double)part;
+        for (int j = 1; j < EPL; ++j) part += __builtin_amdgcn_exp2f(fmaf(x[j], kTkLog2e, -m2));
+        s += (double)part;
+      }
     }
     // candidates (rare once the threshold has risen): skipped when no lane of the wave
     // has one, which the lane maximum alone tells (a NaN is never a candidate)
-    if (__ballot(in && lm >= tf)) {
+    if (__builtin_amdgcn_ballot_w64(lm >= tf)) {  // lanes past the row count nothing below
       int mycnt = 0;
 #pragma unroll
       for (int j = 0; j < EPL; ++j) mycnt += (in && x[j] >= tf) ? 1 : 0;
@@ -336,11 +345,11 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
     radix_select<TB>(s_ck, n, K, s_hist, s_res, t);
     n = compact<TB, CAP>(s_ck, n, s_res[0], (int)s_res[1], &s_cnt, t);
   }
-  // logsumexp of the row
-  float M = m;
+  // logsumexp of the row, in base 2 (M, Mb: the largest m2)
+  float M = m2;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  double sl = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f((m - M) * kTkLog2e);
+  double sl = (m2 == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f(m2 - M);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) sl += __shfl_xor(sl, o, 64);
   if (lane == 0) {
@@ -352,11 +361,11 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
   for (int i = 1; i < kTkThreads / 64; ++i) Mb = fmaxf(Mb, s_m[i]);
   double Sd = 0.0;
   for (int i = 0; i < kTkThreads / 64; ++i)
-    if (s_m[i] != -INFINITY) Sd += s_s[i] * (double)__builtin_amdgcn_exp2f((s_m[i] - Mb) * kTkLog2e);
+    if (s_m[i] != -INFINITY) Sd += s_s[i] * (double)__builtin_amdgcn_exp2f(s_m[i] - Mb);
   const float Sb = (float)Sd;
   const bool finite = Mb > -INFINITY && Mb < INFINITY && Sd == Sd && Sd < (double)INFINITY;
   if (t == 0 && (anybad || !finite || n != K)) atomicOr(flags, 1);
-  if (t == 0 && lse_out) lse_out[row] = Mb + __builtin_amdgcn_logf(Sb) * kTkLn2;
+  if (t == 0 && lse_out) lse_out[row] = (Mb + __builtin_amdgcn_logf(Sb)) * kTkLn2;
   // rank of each selected entry among the K (keys are unique), then write in order
   const float invS = 1.f / Sb;
   for (int i = t; i < n; i += kTkThreads) {
@@ -367,7 +376,7 @@ __global__ __launch_bounds__(kTkThreads) void k_teacher_topk(const void *logits,
     const float xv = T::value((uint32_t)(c >> 32));
     if (rank < K) {
       idx_out[row * K + rank] = (int32_t)ix;
-      p_out[row * K + rank] = __builtin_amdgcn_exp2f((xv - Mb) * kTkLog2e) * invS;
+      p_out[row * K + rank] = __builtin_amdgcn_exp2f(fmaf(xv, kTkLog2e, -Mb)) * invS;
     }
   }
 }
