@@ -25,6 +25,22 @@ PEAK_HBM_GBS = 8000.0
 GEMM_CLASSES = ("fwd_gemm_lse", "bwd_gemm_dz", "dh_gemm", "dw_gemm")
 
 
+def warm_up(step, n, seconds=0.5):
+    """At least n untimed calls of step, and calls for at least `seconds` of wall time:
+    a few short steps do not bring the GPU to its steady clock."""
+    import torch
+    t0 = time.perf_counter()
+    k = 0
+    while k < n or time.perf_counter() - t0 < seconds:
+        out = step()
+        del out
+        k += 1
+        if k % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return k
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,14 +157,7 @@ def bench_topk(args):
         kd._check(lib.kd_teacher_topk(x.data_ptr(), kd.KD_BF16, N, V, K, idx.data_ptr(),
                                       pr.data_ptr(), lse.data_ptr(), ws.data_ptr(), 256, strm))
 
-    # A call takes ~1.5 ms, so a few calls do not bring the GPU to its steady clock:
-    # warm up for at least half a second (and at least `warmup` calls)
-    t0 = time.perf_counter()
-    nw = 0
-    while nw < args.warmup or time.perf_counter() - t0 < 0.5:
-        call()
-        nw += 1
-    torch.cuda.synchronize()
+    warm_up(call, args.warmup)
     kd.profile_read()
     kd.profile_enable(True)
     t0 = time.perf_counter()
@@ -347,10 +356,11 @@ def bench_split(args, kd, torch, cfg, h, W, idx, p, mask, ws):
     """Forward half and backward half timed separately (each over args.steps calls)."""
     g = torch.ones(1, dtype=torch.float32, device="cuda")
     loss, row_lse = kd.fwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws)
-    for _ in range(args.warmup):
+    def fwd_bwd_pair():
         kd.fwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws)
         kd.bwd(h, W, idx, p, row_lse, g, mask, chunk=cfg.chunk, workspace=ws)
-    torch.cuda.synchronize()
+
+    warm_up(fwd_bwd_pair, args.warmup)
     print("[bench] warmup done", file=sys.stderr, flush=True)
     res_half = {}
     for half in ("fwd", "bwd"):
@@ -411,9 +421,7 @@ def bench_shard(args, kd, torch, cfg, h, W, idx, p, mask):
         kd.vocab_shard_fwd(h, Ws, idx, p, 0, cfg.V, chunk=cfg.chunk, workspace=ws)
         kd.vocab_shard_bwd(h, Ws, idx, p, lse, 0, cfg.V, g, mask, chunk=cfg.chunk, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     kd.profile_read()
     kd.profile_enable(True)
     t0 = time.perf_counter()
@@ -498,10 +506,7 @@ def main():
     if args.shard:
         return bench_shard(args, kd, torch, cfg, h, W, idx, p, mask)
 
-    for _ in range(args.warmup):
-        out = step()
-        del out
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
     prof = not args.no_profile
