@@ -8,6 +8,7 @@ Default workload: N=32768 tokens, d=3072, V=128256, K=100, chunk 2048, bf16, pac
 sequences with each sequence's first token masked (synthetic, seeded).
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -48,6 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=2, help="workload id (synth.CONFIGS)")
     ap.add_argument("--N", type=int, default=None, help="override the token count")
+    ap.add_argument("--chunk", type=int, default=None, help="override the chunk size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="token rows of the workload timed through the CPU oracle (a bounded "
@@ -411,6 +413,11 @@ def bench_shard(args, kd, torch, cfg, h, W, idx, p, mask):
     G = args.shard
     Vs = (cfg.V + G - 1) // G
     Ws = W[:Vs].contiguous()
+    # A shard has V/G vocabulary rows, so G times the workload's chunk keeps the chunk's
+    # logits buffer (chunk x V_shard bf16) the size the unsharded call has; --chunk
+    # overrides it.
+    if args.chunk is None:
+        cfg = dataclasses.replace(cfg, chunk=min(cfg.chunk * G, cfg.N))
     ws = torch.empty(kd.workspace_bytes(cfg.N, cfg.d, Vs, cfg.K, cfg.chunk,
                                         kd.KD_BF16 if cfg.dtype == "bf16" else kd.KD_F32),
                      dtype=torch.uint8, device="cuda")
@@ -477,6 +484,8 @@ def main():
     import synth
 
     overrides = {} if args.N is None else {"N": args.N}
+    if args.chunk is not None:
+        overrides["chunk"] = args.chunk
     t_gen = time.perf_counter()
     inp = synth.make(args.config, **overrides)
     cfg = inp.cfg

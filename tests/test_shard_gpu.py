@@ -116,3 +116,62 @@ def test_index_outside_the_vocabulary_is_rejected(torch_cuda):
     with pytest.raises(kd.KDError) as e:
         kd.vocab_shard_fwd(h, W[:1000].contiguous(), idx, p, 0, inp.cfg.V, chunk=64)
     assert e.value.code == 2
+
+
+def test_bench_launch_shard_of_eight(torch_cuda):
+    """The benchmark's shard launch: rows [0, V/8) of the 128256 vocabulary, N = 32768
+    tokens, chunks of 16384 (eight times the unsharded chunk, the same logits-buffer
+    size).  Forward statistics on 256 sampled rows; the backward, given the shard's own
+    logsumexp as lse, for dh on the sampled rows and the shard's whole dW, against the
+    definitions restricted to the shard in float64 (dz = g (mask/count) (M exp(z - lse)
+    - p at the teacher's in-shard tokens))."""
+    import output_head_kl_amd as kd
+    torch = torch_cuda
+    inp = synth.make(2)
+    cfg = inp.cfg
+    V, Vs, chunk = cfg.V, (cfg.V + 7) // 8, 16384
+    h, W, idx, p, mask = to_device(inp, torch)
+    Ws = W[:Vs].contiguous()
+    m, s, pz = kd.vocab_shard_fwd(h, Ws, idx, p, 0, V, chunk=chunk)
+    gm, gs, gp = (to_f64(t, torch) for t in (m, s, pz))
+    del m, s, pz
+    H, Wsh = inp.h64(), inp.W64()[:Vs]
+    rows = synth.subset_rows(cfg, inp.seed, 256)
+    sel = np.zeros(cfg.N, dtype=bool)
+    sel[rows] = True
+    count = int((inp.mask != 0).sum())
+    scale = (inp.mask != 0) / count
+    lse32 = np.empty(cfg.N, dtype=np.float32)
+    stats = {}
+    dW = np.zeros((Vs, cfg.d))
+    dh_rows = {}
+    for r0 in range(0, cfg.N, 1024):
+        r1 = min(cfg.N, r0 + 1024)
+        Z = H[r0:r1] @ Wsh.T
+        mx = Z.max(axis=1)
+        se = np.exp(Z - mx[:, None]).sum(axis=1)
+        lse32[r0:r1] = (mx + np.log(se)).astype(np.float32)
+        ii, pp = inp.idx[r0:r1], inp.p[r0:r1].astype(np.float64)
+        inside = ii < Vs
+        for j in np.nonzero(sel[r0:r1])[0]:
+            zl = np.where(inside[j], Z[j, np.clip(ii[j], 0, Vs - 1)], 0.0)
+            stats[r0 + j] = (mx[j], se[j], float((pp[j] * zl).sum()))
+        dZ = pp.sum(axis=1)[:, None] * np.exp(Z - lse32[r0:r1, None].astype(np.float64))
+        rr = np.broadcast_to(np.arange(r1 - r0)[:, None], ii.shape)
+        np.add.at(dZ, (rr[inside], ii[inside]), -pp[inside])
+        dZ *= scale[r0:r1, None]
+        dW += dZ.T @ H[r0:r1]
+        for j in np.nonzero(sel[r0:r1])[0]:
+            dh_rows[r0 + j] = dZ[j] @ Wsh
+    rm, rs, rpz = (np.array([stats[r][i] for r in rows]) for i in range(3))
+    assert max_abs_rel(gm[rows], rm) < 2e-3
+    assert rel_vec(gs[rows] * np.exp(gm[rows] - rm), rs) < 2e-3
+    assert np.abs(gp[rows] - rpz).max() <= 2e-3 * np.abs(rpz).max() + 1e-6
+    dhp, dWp = kd.vocab_shard_bwd(h, Ws, idx, p, torch.from_numpy(lse32).cuda(), 0, V, None,
+                                  mask, chunk=chunk)
+    torch.cuda.synchronize()
+    e_dh = np.linalg.norm(to_f64(dhp, torch)[rows] - np.array([dh_rows[r] for r in rows]))
+    e_dh /= np.linalg.norm(np.array([dh_rows[r] for r in rows]))
+    e_dW = np.linalg.norm(to_f64(dWp, torch) - dW) / np.linalg.norm(dW)
+    print(f"shard of eight at the bench launch: dh rows {e_dh:.2e}, dW {e_dW:.2e}", flush=True)
+    assert e_dh <= TOL["bf16"]["grad"] and e_dW <= TOL["bf16"]["grad"]
