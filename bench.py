@@ -42,6 +42,27 @@ def warm_up(step, n, seconds=0.5):
     return k
 
 
+def timed_then_profiled(step, steps):
+    """Time `steps` calls of step with nothing else recorded, then run them again with
+    the library's per-launch HIP events on: (ms per call, kernel table of that pass)."""
+    import torch
+
+    import output_head_kl_amd as kd
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    kd.profile_read()
+    kd.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kd.profile_enable(False)
+    return ms, _kernel_table(kd.profile_read(), steps)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,16 +181,7 @@ def bench_topk(args):
                                       pr.data_ptr(), lse.data_ptr(), ws.data_ptr(), 256, strm))
 
     warm_up(call, args.warmup)
-    kd.profile_read()
-    kd.profile_enable(True)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        call()
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    kd.profile_enable(False)
-    kt = _kernel_table(kd.profile_read(), args.steps)
-    ms = el / args.steps * 1e3
+    ms, kt = timed_then_profiled(call, args.steps)
     kern_ms = kt["teacher_topk"]["avg_ms"]
     algo_bytes = N * V * 2 + N * K * 8 + N * 4       # logits once; idx, p and lse written
     achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
@@ -364,21 +376,12 @@ def bench_split(args, kd, torch, cfg, h, W, idx, p, mask, ws):
 
     warm_up(fwd_bwd_pair, args.warmup)
     print("[bench] warmup done", file=sys.stderr, flush=True)
-    res_half = {}
-    for half in ("fwd", "bwd"):
-        kd.profile_read()
-        kd.profile_enable(True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            if half == "fwd":
-                kd.fwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws)
-            else:
-                kd.bwd(h, W, idx, p, row_lse, g, mask, chunk=cfg.chunk, workspace=ws)
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t0
-        kd.profile_enable(False)
-        res_half[half] = (el / args.steps * 1e3, _kernel_table(kd.profile_read(), args.steps))
+    res_half = {
+        "fwd": timed_then_profiled(
+            lambda: kd.fwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws), args.steps),
+        "bwd": timed_then_profiled(
+            lambda: kd.bwd(h, W, idx, p, row_lse, g, mask, chunk=cfg.chunk, workspace=ws),
+            args.steps)}
     fwd_ms, fk = res_half["fwd"]
     bwd_ms, bk = res_half["bwd"]
     ms = fwd_ms + bwd_ms
@@ -429,16 +432,7 @@ def bench_shard(args, kd, torch, cfg, h, W, idx, p, mask):
         kd.vocab_shard_bwd(h, Ws, idx, p, lse, 0, cfg.V, g, mask, chunk=cfg.chunk, workspace=ws)
 
     warm_up(step, args.warmup)
-    kd.profile_read()
-    kd.profile_enable(True)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    kd.profile_enable(False)
-    kt = _kernel_table(kd.profile_read(), args.steps)
-    ms = el / args.steps * 1e3
+    ms, kt = timed_then_profiled(step, args.steps)
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     gem = {k: v for k, v in kt.items() if k in GEMM_CLASSES}
     dom = max(gem, key=lambda k: gem[k]["total_ms_per_step"])
