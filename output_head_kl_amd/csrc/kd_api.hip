@@ -107,15 +107,24 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
   L->V_pad = rup(V, L->tv == kTile ? kTile : 3 * kTile);  // a multiple of 256 and of tv
   L->d_pad = rup(d, kTile);
   L->n_lse = (V + L->tv / 2 - 1) / (L->tv / 2);
-  // Split the vocabulary of the dh GEMM so that two (bf16) or three (fp32) workgroups
-  // per CU run.
+  // Split the vocabulary of the dh GEMM so that its workgroups fill whole rounds of the
+  // slots that run at once (one workgroup per CU in bf16, three in fp32).  Within one
+  // round more splits are more parallel work; past it, a larger split count must fill
+  // its rounds 5 % better than the best smaller one, as each split adds a float32
+  // partial of dh to reduce.
   const int64_t tiles = ((d + L->tv - 1) / L->tv) * (L->C_alloc / kTile);
-  const int64_t target = dtype == KD_BF16 ? 256 : 768;
-  int64_t ns = (target + tiles - 1) / tiles;
+  const int64_t slots = dtype == KD_BF16 ? 256 : 768;
   const int64_t max_by_k = L->V_pad / kTile;  // at least one dz column block per split
-  if (ns > max_by_k) ns = max_by_k;
-  if (ns > 16) ns = 16;
-  if (ns < 1) ns = 1;
+  int64_t ns = 1;
+  double best = 0.0;
+  for (int64_t c = 1; c <= 16 && c <= max_by_k; ++c) {
+    const int64_t wgs = tiles * c, rounds = (wgs + slots - 1) / slots;
+    const double fill = (double)wgs / (double)(rounds * slots);
+    if ((rounds == 1 && fill > best) || fill > best + 0.05) {
+      best = fill;
+      ns = c;
+    }
+  }
   L->k_split = rup((L->V_pad + ns - 1) / ns, kTile);  // splits start on a dz column block
   L->nsplit = (int)((L->V_pad + L->k_split - 1) / L->k_split);
   size_t off = 0;

@@ -72,6 +72,15 @@ def test_wide_logit_range(torch_cuda, dtype):
     _check_full(inp, run(inp, torch_cuda))
 
 
+def test_dh_split_over_several_rounds(torch_cuda):
+    """d = 3136 needs nine 384-row tiles of dh per 256-token tile, so the vocabulary is
+    split seven ways and the dh GEMM runs 504 workgroups, two rounds of the 256 CUs (the
+    last d tile partial); the float32 partials are reduced in order."""
+    inp = synth.make(1, seed=61, N=2048, d=3136, V=16000, K=20, chunk=2048)
+    inp.mask[[1, 1000, 2047]] = 0
+    _check_full(inp, run(inp, torch_cuda))
+
+
 def _uniform_teacher(N, V, K, rng):
     """K distinct uniform indices per row (a permutation when K = V) and probabilities
     from the softmax of sorted N(0, 2) scores, scaled to a mass of 0.9."""
