@@ -515,8 +515,10 @@ def main():
     prof = not args.no_profile
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    out = None
     for _ in range(args.steps):
-        out = step()
+        out = None       # the previous step's outputs go back to the pool first, so the
+        out = step()     # peak below is that of one call
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     loss_val = float(out[0].item())
@@ -531,6 +533,7 @@ def main():
         torch.cuda.synchronize()
         tp = time.perf_counter()
         for _ in range(args.steps):
+            out = None
             out = step()
         torch.cuda.synchronize()
         ms_profiled = (time.perf_counter() - tp) / args.steps * 1e3
