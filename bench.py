@@ -469,8 +469,8 @@ def main():
         bench_topk(args)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
-              "multi-GPU path; see DESIGN.md for how the work would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
+              "multi-GPU path (no collectives or sharding across GPUs).", file=sys.stderr)
         sys.exit(2)
     import torch
 
