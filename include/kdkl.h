@@ -3,11 +3,14 @@
  *
  * The operation is the "fused chunked KL loss" of "Efficient Knowledge
  * Distillation for LLMs: Offline Top-K Logits and a Fused Chunked KL Loss":
- * the student's vocabulary output projection joined to the loss calculation,
- * processed one sequence chunk at a time and recomputed during backpropagation
- * so that the full tokens-by-vocabulary logit tensor is never stored
- * (thorstenmeyerai.com article, TL;DR and infographic "Fuse and chunk" /
- * "Recompute backward"; aimodeling.com article, "Second cut").  The teacher is
+ * the student's vocabulary output projection joined to the loss calculation and
+ * processed one sequence chunk at a time, so that the full tokens-by-vocabulary
+ * logit tensor is never materialised (thorstenmeyerai.com article, TL;DR and
+ * infographic "Fuse and chunk"; aimodeling.com article, "Second cut").  The
+ * pages' autograd form recomputes each chunk's logits during backpropagation
+ * (infographic "Recompute backward"): kd_chunked_kl_bwd does that.  The one-call
+ * kd_chunked_kl_fwd_bwd runs each chunk's backward right after its forward and
+ * takes dz from the exponentials that forward kept for that chunk instead.  The teacher is
  * a cache of its top-K tokens and their probabilities per position
  * (aimodeling.com article, "First cut": top-100 probabilities per token).
  *
@@ -109,7 +112,12 @@ int kd_workspace_bytes_group(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
  *   workspace         256-byte aligned; kd_workspace_bytes(...) bytes for full speed,
  *                     at least kd_workspace_bytes_group(..., 0, ...) bytes
  * Sizes: N >= 0, 1 <= K <= 32768, V >= 1, d >= 8 with d % 8 == 0, chunk >= 1,
- *   d <= 2^20, V <= 2^24, N*d and N*K below 2^62.  N == 0 writes loss = 0 and dW = 0.
+ *   d <= 2^20, V <= 2^24, N*d and N*K below 2^62 (else KD_E_ARG or KD_E_UNSUPPORTED);
+ *   one chunk, min(chunk, N) rows, at most 2^22 rows and 2^31 - 1 teacher entries
+ *   (else KD_E_UNSUPPORTED).  N == 0 writes loss = 0 and dW = 0.
+ * Repeated indices within a row are valid, so K may exceed V: each entry's logit is
+ *   gathered on its own and the probabilities of equal indices add up in dz (the
+ *   sparse term is a scatter-add).  Each index must lie in [0, V).
  * chunk is the number of token rows whose logits are live at once; the last
  *   chunk may be partial; results do not depend on it beyond float rounding.
  *   Each chunk's backward runs right after its forward, while the chunk's logits
@@ -131,6 +139,42 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype,
                           float *loss, void *dh, float *dW,
                           float *row_loss, float *row_lse, float *zg,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kd_chunked_kl_fwd_bwd_f32dh -- kd_chunked_kl_fwd_bwd with dh written in float32.
+ *
+ * The pages' loss is an autograd function of the hidden states (codewithpapers.app
+ * record: _SparseKLHiddenStatesChunkedFunction); its backward receives the upstream
+ * gradient g of the loss only after the forward.  A caller that wants the one-call speed
+ * in that setting runs this call in its forward (the gradients for g = 1) and
+ * kd_scale_grads in its backward.  dh here is [N, d] float32 (16-byte aligned), the
+ * float32 sums that kd_chunked_kl_fwd_bwd rounds to dtype; every other argument, output,
+ * workspace size, stream behaviour and error as kd_chunked_kl_fwd_bwd, whose loss, dW and
+ * row outputs it reproduces bit for bit.
+ */
+int kd_chunked_kl_fwd_bwd_f32dh(const void *h, const void *W, int32_t dtype,
+                                const int32_t *topk_idx, const float *topk_p,
+                                const uint8_t *loss_mask,
+                                int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                                float *loss, float *dh, float *dW,
+                                float *row_loss, float *row_lse, float *zg,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kd_scale_grads -- apply the upstream gradient g of the loss to gradients computed
+ * for g = 1 (by kd_chunked_kl_fwd_bwd_f32dh): by the chain rule dL'/dh = g * dL/dh
+ * and dL'/dW = g * dL/dW for L' = g * L.
+ *   grad_loss [1]    float32  device   g
+ *   dh_f32    [N, d] float32  device   input, 16-byte aligned
+ *   dh        [N, d] dtype    device   output: g * dh_f32 rounded once to dtype (RNE);
+ *                                      may be dh_f32 itself only when dtype is KD_F32
+ *   dW        [V, d] float32  device   scaled in place (left untouched when g == 1, where
+ *                                      the product is exact)
+ * All work is enqueued on stream; no synchronisation.  Errors: KD_E_ARG for a null
+ * required pointer, a misaligned one, an unknown dtype or a negative size.
+ */
+int kd_scale_grads(const float *grad_loss, const float *dh_f32, void *dh, int32_t dtype,
+                   int64_t N, int64_t d, float *dW, int64_t V, void *stream);
 
 /*
  * kd_chunked_kl_fwd -- the forward half: loss and the per-token logsumexp.

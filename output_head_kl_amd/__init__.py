@@ -13,7 +13,7 @@ import os
 from typing import Optional
 
 __all__ = ["KDError", "library_path", "workspace_bytes", "fwd_bwd", "fwd", "bwd",
-           "chunked_kl_loss", "teacher_topk", "vocab_shard_fwd", "vocab_shard_combine",
+           "chunked_kl_loss", "scale_grads", "teacher_topk", "vocab_shard_fwd", "vocab_shard_combine",
            "vocab_shard_bwd", "profile_enable", "profile_read", "profile_classes", "KD_F32",
            "KD_BF16"]
 
@@ -52,6 +52,11 @@ def _lib():
     lib.kd_chunked_kl_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
                                           vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_fwd_bwd.restype = ctypes.c_int
+    lib.kd_chunked_kl_fwd_bwd_f32dh.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32,
+                                                i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_chunked_kl_fwd_bwd_f32dh.restype = ctypes.c_int
+    lib.kd_scale_grads.argtypes = [vp, vp, vp, i32, i64, i64, vp, i64, vp]
+    lib.kd_scale_grads.restype = ctypes.c_int
     lib.kd_chunked_kl_fwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
                                       vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_fwd.restype = ctypes.c_int
@@ -117,6 +122,16 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _on_device(dev, **tensors):
+    """Every tensor argument must live on ``dev``, a CUDA device: the library receives
+    bare addresses and would read a host or another GPU's address as its own."""
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be CUDA tensors, got device {dev}")
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != dev):
+            raise ValueError(f"{name} is on {t.device}; every tensor argument must be on {dev}")
+
+
 def _prep(h, W, topk_idx, topk_p, loss_mask):
     """Checks dtypes, shapes and contiguity; returns (dtype code, N, d, V, K, mask)."""
     import torch
@@ -125,6 +140,7 @@ def _prep(h, W, topk_idx, topk_p, loss_mask):
         raise TypeError("h and W must have the same dtype")
     if topk_idx.dtype != torch.int32 or topk_p.dtype != torch.float32:
         raise TypeError("topk_idx must be int32 and topk_p float32")
+    _on_device(h.device, h=h, W=W, topk_idx=topk_idx, topk_p=topk_p, loss_mask=loss_mask)
     tensors = [h, W, topk_idx, topk_p] + ([loss_mask] if loss_mask is not None else [])
     for t in tensors:
         if not t.is_contiguous():
@@ -147,7 +163,16 @@ def _workspace(workspace, N, d, V, K, chunk, dt, dev, dw_group_tokens=None):
     if workspace is None:
         workspace = torch.empty(max(workspace_bytes(N, d, V, K, chunk, dt, dw_group_tokens), 256),
                                 dtype=torch.uint8, device=dev)
+    else:
+        _check_workspace(workspace, dev)
     return workspace
+
+
+def _check_workspace(workspace, dev):
+    import torch
+    _on_device(dev, workspace=workspace)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
 
 
 def _stream(stream, dev):
@@ -156,7 +181,8 @@ def _stream(stream, dev):
 
 
 def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: bool = False,
-            workspace=None, stream=None, dw_group_tokens: Optional[int] = None):
+            workspace=None, stream=None, dw_group_tokens: Optional[int] = None,
+            dh_float32: bool = False):
     """Mean top-K KL loss with its gradients, computed chunk by chunk on the GPU.
 
     Args (torch CUDA tensors, contiguous):
@@ -167,6 +193,8 @@ def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: boo
       workspace: optional uint8 tensor; the call takes the largest dW group it holds.
       dw_group_tokens: size of the workspace allocated when none is given (see
         ``workspace_bytes``); None is the default, full-speed group.
+      dh_float32: return dh as the float32 sums, not rounded to h's dtype
+        (kd_chunked_kl_fwd_bwd_f32dh), e.g. for ``scale_grads``.
     Returns (loss[1] f32, dh [N, d] dtype, dW [V, d] f32) and, with ``rows``,
     (row_loss [N], row_lse [N], zg [N, K]) as float32.
     """
@@ -175,14 +203,15 @@ def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: boo
     dev = h.device
     workspace = _workspace(workspace, N, d, V, K, chunk, dt, dev, dw_group_tokens)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
-    dh = torch.empty((N, d), dtype=h.dtype, device=dev)
+    dh = torch.empty((N, d), dtype=torch.float32 if dh_float32 else h.dtype, device=dev)
     dW = torch.empty((V, d), dtype=torch.float32, device=dev)
     row_loss = row_lse = zg = None
     if rows:
         row_loss = torch.empty(N, dtype=torch.float32, device=dev)
         row_lse = torch.empty(N, dtype=torch.float32, device=dev)
         zg = torch.empty((N, K), dtype=torch.float32, device=dev)
-    _check(_lib().kd_chunked_kl_fwd_bwd(
+    call = _lib().kd_chunked_kl_fwd_bwd_f32dh if dh_float32 else _lib().kd_chunked_kl_fwd_bwd
+    _check(call(
         _ptr(h), _ptr(W), dt, _ptr(topk_idx), _ptr(topk_p), _ptr(loss_mask), N, d, V, K, chunk,
         _ptr(loss), _ptr(dh), _ptr(dW), _ptr(row_loss), _ptr(row_lse), _ptr(zg),
         _ptr(workspace), workspace.numel(), _stream(stream, dev)))
@@ -223,6 +252,7 @@ def bwd(h, W, topk_idx, topk_p, row_lse, grad_loss=None, loss_mask=None, chunk: 
     import torch
     dt, N, d, V, K, loss_mask = _prep(h, W, topk_idx, topk_p, loss_mask)
     dev = h.device
+    _on_device(dev, row_lse=row_lse, grad_loss=grad_loss)
     if row_lse.dtype != torch.float32 or tuple(row_lse.shape) != (N,) or not row_lse.is_contiguous():
         raise ValueError("row_lse must be a contiguous float32 tensor of shape [N]")
     if grad_loss is None:
@@ -241,8 +271,59 @@ def bwd(h, W, topk_idx, topk_p, row_lse, grad_loss=None, loss_mask=None, chunk: 
     return dh, dW
 
 
-def _autograd_function():
+def scale_grads(grad_loss, dh_f32, dW, dtype=None, stream=None):
+    """Gradients for an upstream gradient g of the loss from those for g = 1
+    (kd_scale_grads): returns dh = g * dh_f32 rounded once to ``dtype`` (default
+    float32) and scales ``dW`` in place (untouched when g == 1), which it also returns."""
     import torch
+    dev = dh_f32.device
+    _on_device(dev, grad_loss=grad_loss, dh_f32=dh_f32, dW=dW)
+    dtype = torch.float32 if dtype is None else dtype
+    dt = KD_BF16 if dtype == torch.bfloat16 else KD_F32 if dtype == torch.float32 else None
+    if dt is None:
+        raise TypeError("dh must be bfloat16 or float32")
+    if (dh_f32.dtype != torch.float32 or dW.dtype != torch.float32 or dh_f32.dim() != 2
+            or dW.dim() != 2 or dW.shape[1] != dh_f32.shape[1] or not dh_f32.is_contiguous()
+            or not dW.is_contiguous()):
+        raise ValueError("dh_f32 [N, d] and dW [V, d] must be contiguous float32")
+    if grad_loss.dtype != torch.float32 or grad_loss.numel() != 1:
+        raise TypeError("grad_loss must be a one-element float32 tensor")
+    g = grad_loss.reshape(1).contiguous()
+    N, d = dh_f32.shape
+    dh = torch.empty((N, d), dtype=dtype, device=dev)
+    _check(_lib().kd_scale_grads(_ptr(g), _ptr(dh_f32), _ptr(dh), dt, N, d, _ptr(dW),
+                                 dW.shape[0], _stream(stream, dev)))
+    return dh, dW
+
+
+def _autograd_functions():
+    import torch
+
+    class ChunkedKLFused(torch.autograd.Function):
+        """The loss as an autograd function of h and W at the one-call speed: the forward
+        runs the one-call loss and gradients for g = 1 (dh kept in float32) and holds
+        them; the backward applies the upstream gradient g on the device."""
+
+        @staticmethod
+        def forward(ctx, h, W, topk_idx, topk_p, loss_mask, chunk):
+            loss, dh32, dW = fwd_bwd(h, W, topk_idx, topk_p, loss_mask, chunk,
+                                     dh_float32=True)
+            ctx.grads = (dh32, dW)
+            ctx.h_dtype = h.dtype
+            return loss.view(())
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            if ctx.grads is None:
+                raise RuntimeError("the fused chunked KL loss can be differentiated once; "
+                                   "use mode='recompute' to call backward again")
+            dh32, dW = ctx.grads
+            ctx.grads = None
+            g = grad_out.detach().reshape(1).to(torch.float32).contiguous()
+            dh, dW = scale_grads(g, dh32, dW, ctx.h_dtype)
+            del dh32
+            # dW is float32; autograd converts it to W's dtype if they differ
+            return dh, dW, None, None, None, None
 
     class ChunkedKL(torch.autograd.Function):
         """The loss as an autograd function of h and W: the forward keeps only the
@@ -263,18 +344,28 @@ def _autograd_function():
             # dW is float32; autograd converts it to W's dtype if they differ
             return dh, dW, None, None, None, None
 
-    return ChunkedKL
+    return {"fused": ChunkedKLFused, "recompute": ChunkedKL}
 
 
 _CHUNKED_KL = None
 
 
-def chunked_kl_loss(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048):
-    """Mean top-K KL loss as a differentiable scalar of h and W (torch autograd)."""
+def chunked_kl_loss(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048,
+                    mode: str = "fused"):
+    """Mean top-K KL loss as a differentiable scalar of h and W (torch autograd).
+
+    mode "fused" (default): the forward computes the loss and both gradients in one
+      call and holds dh (float32) and dW until the backward, which scales them by the
+      upstream gradient on the device: the one-call speed, with those two tensors
+      alive between forward and backward.  Differentiable once.
+    mode "recompute": the forward keeps only the per-token logsumexp; the backward
+      recomputes the logits chunk by chunk (the pages' autograd form)."""
     global _CHUNKED_KL
     if _CHUNKED_KL is None:
-        _CHUNKED_KL = _autograd_function()
-    return _CHUNKED_KL.apply(h, W, topk_idx, topk_p, loss_mask, chunk)
+        _CHUNKED_KL = _autograd_functions()
+    if mode not in _CHUNKED_KL:
+        raise ValueError(f"mode must be 'fused' or 'recompute', not {mode!r}")
+    return _CHUNKED_KL[mode].apply(h, W, topk_idx, topk_p, loss_mask, chunk)
 
 
 def teacher_topk(logits, K: int = 100, lse: bool = True, workspace=None, stream=None):
@@ -286,10 +377,13 @@ def teacher_topk(logits, K: int = 100, lse: bool = True, workspace=None, stream=
     dt = _dtype_code(logits)
     N, V = logits.shape
     dev = logits.device
+    _on_device(dev, logits=logits)
     if workspace is None:
         out = ctypes.c_size_t(0)
         _check(_lib().kd_topk_workspace_bytes(ctypes.byref(out)))
         workspace = torch.empty(int(out.value), dtype=torch.uint8, device=dev)
+    else:
+        _check_workspace(workspace, dev)
     idx = torch.empty((N, K), dtype=torch.int32, device=dev)
     p = torch.empty((N, K), dtype=torch.float32, device=dev)
     row_lse = torch.empty(N, dtype=torch.float32, device=dev) if lse else None
@@ -323,15 +417,26 @@ def vocab_shard_combine(shard_max, shard_sumexp, shard_pz, topk_p, loss_mask=Non
     G, N = shard_max.shape
     K = topk_p.shape[1]
     dev = shard_max.device
+    _on_device(dev, shard_max=shard_max, shard_sumexp=shard_sumexp, shard_pz=shard_pz,
+               topk_p=topk_p, loss_mask=loss_mask)
     for t in (shard_max, shard_sumexp, shard_pz, topk_p):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError("shard statistics and topk_p must be contiguous float32")
-    if loss_mask is not None and loss_mask.dtype == torch.bool:
-        loss_mask = loss_mask.view(torch.uint8)
+    if (tuple(shard_sumexp.shape) != (G, N) or tuple(shard_pz.shape) != (G, N)
+            or topk_p.dim() != 2 or topk_p.shape[0] != N):
+        raise ValueError("shard statistics must be [G, N] and topk_p [N, K]")
+    if loss_mask is not None:
+        if loss_mask.dtype == torch.bool:
+            loss_mask = loss_mask.view(torch.uint8)
+        if (loss_mask.dtype != torch.uint8 or tuple(loss_mask.shape) != (N,)
+                or not loss_mask.is_contiguous()):
+            raise ValueError("loss_mask must be contiguous uint8/bool of shape [N]")
     if workspace is None:
         out = ctypes.c_size_t(0)
         _check(_lib().kd_vocab_shard_combine_workspace_bytes(N, ctypes.byref(out)))
         workspace = torch.empty(int(out.value), dtype=torch.uint8, device=dev)
+    else:
+        _check_workspace(workspace, dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     row_lse = torch.empty(N, dtype=torch.float32, device=dev)
     row_loss = torch.empty(N, dtype=torch.float32, device=dev)
@@ -349,8 +454,13 @@ def vocab_shard_bwd(h, W_shard, topk_idx, topk_p, row_lse, v_offset: int, V_tota
     import torch
     dt, N, d, Vs, K, loss_mask = _prep(h, W_shard, topk_idx, topk_p, loss_mask)
     dev = h.device
+    _on_device(dev, row_lse=row_lse, grad_loss=grad_loss)
+    if row_lse.dtype != torch.float32 or tuple(row_lse.shape) != (N,) or not row_lse.is_contiguous():
+        raise ValueError("row_lse must be a contiguous float32 tensor of shape [N]")
     if grad_loss is None:
         grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
+    if grad_loss.dtype != torch.float32 or grad_loss.numel() != 1:
+        raise TypeError("grad_loss must be a one-element float32 tensor")
     grad_loss = grad_loss.reshape(1).contiguous()
     workspace = _workspace(workspace, N, d, Vs, K, chunk, dt, dev)
     dh = torch.empty((N, d), dtype=torch.float32, device=dev)

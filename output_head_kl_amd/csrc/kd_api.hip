@@ -7,7 +7,9 @@
 // indices, logsumexp + loss, dz, sparse correction of dz, dh GEMM + reduction, dW GEMM.
 // The fused call takes dz from the exp(z - max) its forward GEMM kept in the dz buffer
 // (one streaming rescale once the logsumexp is known); the backward-only call recomputes
-// the logits with a second GEMM.  Only one chunk's dz (in two layouts) is live.
+// the logits with a second GEMM.  One chunk's dz is live, plus its token-contiguous copy
+// for the chunks of one dW group (as many as the workspace passed holds, 16384 tokens at
+// most; one chunk with the smallest workspace).
 #include "kd_internal.h"
 #include "kdkl.h"
 
@@ -73,6 +75,13 @@ int check_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32
   const int64_t lim = (int64_t)1 << 62;
   if (N > 0 && (N > lim / d || N > lim / K)) return fail(KD_E_ARG, "N too large");
   if (V > lim / d) return fail(KD_E_ARG, "V*d too large");
+  // Token offsets inside a chunk (c * 256 in the token-blocked layouts) and the chunk's
+  // teacher-hit count (rows * K bucket entries) are 32-bit in the kernels.
+  const int64_t rows = chunk < (N > 0 ? N : 1) ? chunk : (N > 0 ? N : 1);
+  if (rows > ((int64_t)1 << 22) || rows * K > (int64_t)0x7FFFFFFF)
+    return fail(KD_E_UNSUPPORTED,
+                "min(chunk, N) = %lld rows per chunk: at most 2^22 rows and 2^31 - 1 teacher "
+                "entries per chunk", (long long)rows);
   return KD_OK;
 }
 
@@ -210,7 +219,8 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
         const float *topk_p, const uint8_t *loss_mask, int64_t N, int64_t d, int64_t V, int32_t K,
         int64_t chunk, float *loss, void *dh, float *dW, float *row_loss, float *row_lse,
         float *zg, const float *lse_in, const float *grad_loss, void *workspace,
-        size_t workspace_bytes, void *stream_v, const ShardArgs &sh = ShardArgs()) {
+        size_t workspace_bytes, void *stream_v, const ShardArgs &sh = ShardArgs(),
+        bool dh_f32 = false) {
   g_err[0] = 0;
   int rc = check_sizes(N, d, V, K, chunk, dtype);
   if (rc != KD_OK) return rc;
@@ -274,7 +284,8 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
   unsigned *bent = (unsigned *)(ws + L.off_bent);
   int32_t *idxloc = (int32_t *)(ws + L.off_idxloc);
   const int64_t es = dtype == KD_BF16 ? 2 : 4;
-  const int64_t es_dh = mode == M_SBWD ? 4 : es;  // a shard's dh partial stays float32
+  // a shard's dh partial, and dh for an upstream gradient applied later, stay float32
+  const int64_t es_dh = (mode == M_SBWD || dh_f32) ? 4 : es;
 
   if (N == 0) {
     if (fwd && !shard) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
@@ -375,7 +386,7 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
     LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, WT, rows, d, V, L.V_pad, L.nsplit,
                                               L.k_split, dhpart, L.d_pad, L.C_alloc, stream));
     LAUNCH(kd::KC_DH_REDUCE,
-           kd::launch_dh_reduce(mode == M_SBWD ? (int)KD_F32 : dtype, dhpart, L.nsplit, L.C_alloc,
+           kd::launch_dh_reduce(es_dh == 4 ? (int)KD_F32 : dtype, dhpart, L.nsplit, L.C_alloc,
                                 L.d_pad, rows, d, (char *)dh + c0 * d * es_dh, stream));
     if (ht_c)
       LAUNCH(kd::KC_TRANSPOSE,
@@ -404,6 +415,38 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
                           size_t workspace_bytes, void *stream) {
   return run(M_FUSED, h, W, dtype, topk_idx, topk_p, loss_mask, N, d, V, K, chunk, loss, dh, dW,
              row_loss, row_lse, zg, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kd_chunked_kl_fwd_bwd_f32dh(const void *h, const void *W, int32_t dtype,
+                                const int32_t *topk_idx, const float *topk_p,
+                                const uint8_t *loss_mask, int64_t N, int64_t d, int64_t V,
+                                int32_t K, int64_t chunk, float *loss, float *dh, float *dW,
+                                float *row_loss, float *row_lse, float *zg, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  return run(M_FUSED, h, W, dtype, topk_idx, topk_p, loss_mask, N, d, V, K, chunk, loss, dh, dW,
+             row_loss, row_lse, zg, nullptr, nullptr, workspace, workspace_bytes, stream,
+             ShardArgs(), true);
+}
+
+int kd_scale_grads(const float *grad_loss, const float *dh_f32, void *dh, int32_t dtype,
+                   int64_t N, int64_t d, float *dW, int64_t V, void *stream_v) {
+  g_err[0] = 0;
+  if (dtype != KD_F32 && dtype != KD_BF16) return fail(KD_E_ARG, "dtype %d unknown", dtype);
+  if (N < 0 || d < 1 || V < 0) return fail(KD_E_ARG, "need N >= 0, d >= 1, V >= 0");
+  const int64_t lim = (int64_t)1 << 62;
+  if (N > lim / d || V > lim / d) return fail(KD_E_ARG, "N*d or V*d too large");
+  if (!grad_loss) return fail(KD_E_ARG, "grad_loss is required");
+  if (N > 0 && (!dh_f32 || !dh)) return fail(KD_E_ARG, "dh_f32 and dh are required when N > 0");
+  if (V > 0 && !dW) return fail(KD_E_ARG, "dW is required when V > 0");
+  auto mis = [](const void *p, uintptr_t a) { return p && ((uintptr_t)p % a) != 0; };
+  if (mis(dh_f32, 16) || mis(dh, 16) || mis(dW, 16))
+    return fail(KD_E_ARG, "dh_f32, dh and dW must be 16-byte aligned");
+  if (mis(grad_loss, 4)) return fail(KD_E_ARG, "grad_loss must be 4-byte aligned");
+  if (N * d + V * d == 0) return KD_OK;
+  hipStream_t stream = (hipStream_t)stream_v;
+  LAUNCH(kd::KC_MISC, kd::launch_scale_grads(dtype, grad_loss, dh_f32, dh, N * d, dW, V * d,
+                                             stream));
+  return KD_OK;
 }
 
 int kd_chunked_kl_fwd(const void *h, const void *W, int32_t dtype, const int32_t *topk_idx,

@@ -101,6 +101,10 @@ hipError_t launch_row_scale(const float *p_c, const uint8_t *mask_c, int64_t row
                             hipStream_t s);
 hipError_t launch_accum_loss(const double *rowterm, int64_t rows, double *acc, hipStream_t s);
 hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s);
+// dh_out = g[0] * dh32 rounded once to dtype (bf16 RNE or fp32), dW *= g[0] in place (dW
+// untouched when g[0] == 1); dh32 and dW 16-byte aligned.
+hipError_t launch_scale_grads(int dtype, const float *g, const float *dh32, void *dh_out,
+                              int64_t n_dh, float *dW, int64_t n_dW, hipStream_t s);
 // dz is stored as blocks of 256 vocabulary columns: element (c, v) at
 // dz[(v / 256) * C_alloc * 256 + c * 256 + v % 256].
 // bf16 also writes dzT, the same values in the token-blocked layout (tst = V_pad * 256)

@@ -1,17 +1,22 @@
 // gfx950 kernels of the fused, chunked top-K KL loss.
 //
-// Per token chunk (see kd_api.hip for the sequence):
-//   buckets        the chunk's teacher hits sorted by 256 x 256 output tile;
+// Per token chunk (kd_api.hip enqueues the sequence):
+//   buckets        the chunk's teacher hits sorted by output tile of the logits GEMM;
 //   forward GEMM   z^T tile = W_tile . h_tile^T on MFMA, epilogue: per-token max and
-//                  sum of exp over the tile's vocabulary rows, and z gathered at the
-//                  tile's teacher hits (no logits stored);
-//   combine        logsumexp over the tiles, per-token loss;
-//   backward GEMM  z recomputed, epilogue: dz = (mask/count) * M * exp(z - lse), bf16;
+//                  sum of exp over each 192-row vocabulary group, z gathered at the
+//                  tile's teacher hits, and (one-call form) u = exp(z - max) kept as
+//                  bf16 in the chunk's dz buffer; no logits are stored;
+//   combine        logsumexp over the groups, per-token loss;
+//   dz             one-call form: a streaming rescale of u into dz = (mask/count) * M *
+//                  exp(z - lse), as each chunk's backward follows its forward; the
+//                  backward-only call recomputes z with a second GEMM whose epilogue
+//                  forms the same dz (thorstenmeyerai.com infographic, "Recompute
+//                  backward");
 //   scatter        dz -= (mask/count) * p at the teacher's indices;
 //   dh GEMM        dh = dz . W (split over the vocabulary, fp32 partials, then reduced);
-//   dW GEMM        dW += dz^T . h (fp32 read-modify-write).
-// "Recompute backward: repeat projection work during backpropagation to save memory"
-// (thorstenmeyerai.com infographic); only one chunk's dz is ever live.
+//   dW GEMM        dW += dz^T . h over a group of chunks (fp32 read-modify-write).
+// The dz buffer holds one chunk; its token-contiguous copy for the dW GEMM holds the
+// chunks of one dW group (one chunk with the smallest workspace).
 #include "kd_internal.h"
 
 #include <cstdint>
@@ -1800,6 +1805,61 @@ __global__ void k_finalize(const double *acc, long long count, float *loss) {
 
 hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s) {
   hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, s, acc, (long long)count, loss);
+  return hipGetLastError();
+}
+
+// Upstream gradient of the loss applied to gradients computed for g = 1: dh_out =
+// g * dh32 rounded once to the output type, and dW *= g in place.  g is read on the device;
+// with g == 1 the product is exact, so dW is left alone (no traffic) and dh_out is dh32
+// rounded.  Four elements per thread (16-byte loads; the tail element by element).
+template <int DT>
+__global__ __launch_bounds__(256) void k_scale_grads(const float *g, const float *dh32,
+                                                     void *dh_out, long long n_dh, float *dW,
+                                                     long long n_dW) {
+  const float gv = g[0];
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  const long long t0 = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  for (long long q = t0; q * 4 < n_dh; q += stride) {
+    const long long i = q * 4;
+    if (i + 4 <= n_dh) {
+      const f32x4 x = *(const f32x4 *)(dh32 + i);
+      if (DT == 1) {
+        *(u32x2 *)((unsigned short *)dh_out + i) =
+            u32x2{pack_bf16x2(gv * x[0], gv * x[1]), pack_bf16x2(gv * x[2], gv * x[3])};
+      } else {
+        *(f32x4 *)((float *)dh_out + i) = f32x4{gv * x[0], gv * x[1], gv * x[2], gv * x[3]};
+      }
+    } else {
+      for (long long j = i; j < n_dh; ++j) {
+        if (DT == 1) ((unsigned short *)dh_out)[j] = f32_to_bf16(gv * dh32[j]);
+        else ((float *)dh_out)[j] = gv * dh32[j];
+      }
+    }
+  }
+  if (gv == 1.f) return;
+  for (long long q = t0; q * 4 < n_dW; q += stride) {
+    const long long i = q * 4;
+    if (i + 4 <= n_dW) {
+      f32x4 x = *(const f32x4 *)(dW + i);
+      *(f32x4 *)(dW + i) = f32x4{gv * x[0], gv * x[1], gv * x[2], gv * x[3]};
+    } else {
+      for (long long j = i; j < n_dW; ++j) dW[j] *= gv;
+    }
+  }
+}
+
+hipError_t launch_scale_grads(int dtype, const float *g, const float *dh32, void *dh_out,
+                              int64_t n_dh, float *dW, int64_t n_dW, hipStream_t s) {
+  const long long q = ((n_dh > n_dW ? n_dh : n_dW) + 3) / 4;
+  int blocks = (int)((q + 255) / 256);
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_scale_grads<1>, dim3(blocks), dim3(256), 0, s, g, dh32, dh_out,
+                       (long long)n_dh, dW, (long long)n_dW);
+  else
+    hipLaunchKernelGGL(k_scale_grads<0>, dim3(blocks), dim3(256), 0, s, g, dh32, dh_out,
+                       (long long)n_dh, dW, (long long)n_dW);
   return hipGetLastError();
 }
 

@@ -93,6 +93,8 @@ def test_workspace_for_a_smaller_dw_group(lib):
     ((-1, 16, 100, 4, 8, 1), E_ARG),             # N < 0
     ((10, 16, 100, 4, 8, 7), E_ARG),             # unknown dtype
     ((10, 16, 100, 70000, 8, 1), E_UNSUPPORTED),  # K too large
+    ((1 << 23, 16, 100, 4, 1 << 23, 1), E_UNSUPPORTED),   # 2^23 rows in one chunk
+    ((1 << 22, 16, 100, 1024, 1 << 22, 1), E_UNSUPPORTED),  # 2^32 teacher entries per chunk
 ])
 def test_workspace_query_rejects_bad_sizes(lib, args, code):
     out = ctypes.c_size_t(0)
@@ -128,10 +130,30 @@ def _call(lib, **kw):
     (dict(d=60), E_UNSUPPORTED),
     (dict(chunk=0), E_ARG),
     (dict(wsb=1000), E_WORKSPACE),
+    (dict(N=(1 << 22) + 1, chunk=1 << 30), E_UNSUPPORTED),  # one chunk above 2^22 rows
 ])
 def test_entry_point_rejects_bad_calls_on_host(lib, kw, code):
     assert _call(lib, **kw) == code
     assert lib.kd_last_error()
+
+
+def test_rows_per_chunk_limit_is_on_the_chunk_not_the_batch(lib):
+    """A chunk above the batch means one chunk of N rows: the 2^22-row limit applies to
+    min(chunk, N), so a huge chunk over a small batch and a huge batch in small chunks
+    are both accepted."""
+    out = ctypes.c_size_t(0)
+    assert lib.kd_workspace_bytes(1000, 16, 100, 4, 1 << 40, 1, ctypes.byref(out)) == OK
+    assert lib.kd_workspace_bytes(1 << 30, 16, 100, 4, 4096, 1, ctypes.byref(out)) == OK
+    assert lib.kd_workspace_bytes(1 << 22, 16, 100, 4, 1 << 22, 1, ctypes.byref(out)) == OK
+
+
+def test_more_teacher_entries_than_vocabulary_is_accepted(lib):
+    """K > V is valid: a row then repeats indices, whose probabilities add up in the
+    gradient (scatter-add) while the gather reads each entry; only the range of each
+    index is checked (on the device)."""
+    out = ctypes.c_size_t(0)
+    assert lib.kd_workspace_bytes(64, 64, 10, 40, 32, 1, ctypes.byref(out)) == OK
+    assert _call(lib, V=10, K=40, wsb=1000) == E_WORKSPACE   # passes every size check
 
 
 def test_workspace_too_small_reports_needed_size(lib):
@@ -256,3 +278,57 @@ def _call_shard_fwd(lib, **kw):
 def test_shard_forward_rejects_bad_shards_on_host(lib, kw, code):
     assert _call_shard_fwd(lib, **kw) == code
     assert lib.kd_last_error()
+
+
+def _call_f32dh(lib, **kw):
+    base = dict(h=0x100000, W=0x200000, dtype=1, idx=0x300000, p=0x400000, mask=None, N=64,
+                d=64, V=1000, K=4, chunk=32, loss=0x500000, dh=0x600000, dW=0x700000,
+                row_loss=None, row_lse=None, zg=None, ws=0x800000, wsb=1 << 40, stream=None)
+    base.update(kw)
+    b = base
+    return lib.kd_chunked_kl_fwd_bwd_f32dh(
+        b["h"], b["W"], b["dtype"], b["idx"], b["p"], b["mask"], b["N"], b["d"], b["V"],
+        b["K"], b["chunk"], b["loss"], b["dh"], b["dW"], b["row_loss"], b["row_lse"], b["zg"],
+        b["ws"], b["wsb"], b["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dh=None), E_ARG),
+    (dict(dh=0x600004), E_ARG),      # float32 dh still 16-byte aligned
+    (dict(loss=None), E_ARG),
+    (dict(d=60), E_UNSUPPORTED),
+    (dict(wsb=1000), E_WORKSPACE),
+])
+def test_float32_dh_entry_rejects_bad_calls_on_host(lib, kw, code):
+    assert _call_f32dh(lib, **kw) == code
+    assert lib.kd_last_error()
+
+
+def _call_scale(lib, **kw):
+    base = dict(g=0x100000, dh32=0x200000, dh=0x300000, dtype=1, N=64, d=64, dW=0x400000,
+                V=1000, stream=None)
+    base.update(kw)
+    b = base
+    return lib.kd_scale_grads(b["g"], b["dh32"], b["dh"], b["dtype"], b["N"], b["d"], b["dW"],
+                              b["V"], b["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=None), E_ARG),
+    (dict(dh32=None), E_ARG),
+    (dict(dh=None), E_ARG),
+    (dict(dW=None), E_ARG),
+    (dict(dtype=5), E_ARG),
+    (dict(N=-1), E_ARG),
+    (dict(d=0), E_ARG),
+    (dict(dh32=0x200008), E_ARG),    # not 16-byte aligned
+    (dict(dW=0x400004), E_ARG),
+    (dict(g=0x100002), E_ARG),
+])
+def test_scale_grads_rejects_bad_calls_on_host(lib, kw, code):
+    assert _call_scale(lib, **kw) == code
+    assert lib.kd_last_error()
+
+
+def test_scale_grads_with_nothing_to_scale_does_nothing(lib):
+    assert _call_scale(lib, N=0, V=0, dh32=None, dh=None, dW=None) == OK
