@@ -158,3 +158,77 @@ def test_split_rejects_invalid_entries_without_writing(torch_cuda):
     torch.cuda.synchronize()
     assert rc == 2
     assert float(dh.min()) == 7.0 and float(dW.max()) == 7.0
+
+
+@pytest.mark.parametrize("dtype,g", [("bf16", 3.0), ("f32", -2.5)])
+def test_fused_autograd_mode_matches_oracle(torch_cuda, dtype, g):
+    """chunked_kl_loss(mode='fused'): the forward runs the one-call loss and gradients
+    (dh kept in float32), the backward applies the upstream gradient g on the device
+    (kd_scale_grads); the gradients are g times the oracle's, and agree with the
+    recompute mode's."""
+    import output_head_kl_amd as kd
+    torch = torch_cuda
+    inp = synth.make(1, seed=29, N=500, d=256, V=5000, K=16, chunk=192, dtype=dtype)
+    inp.mask[[0, 77, 499]] = 0
+    ref = oracle.forward_backward(inp.h64(), inp.W64(), inp.idx, inp.p, inp.mask)
+    tol = TOL[dtype]
+    grads = {}
+    for mode in ("fused", "recompute"):
+        h, W, idx, p, mask = to_device(inp, torch)
+        h = h.clone().requires_grad_(True)
+        W = W.clone().requires_grad_(True)
+        loss = kd.chunked_kl_loss(h, W, idx, p, mask, chunk=192, mode=mode)
+        (g * loss).backward()
+        torch.cuda.synchronize()
+        assert loss.dim() == 0 and rel(float(loss), ref["loss"]) <= tol["loss"]
+        assert h.grad.dtype == h.dtype and W.grad.dtype == W.dtype
+        grads[mode] = (to_f64(h.grad, torch), to_f64(W.grad, torch))
+        errs = dict(dh=grad_err(dtype, grads[mode][0], g * ref["dh"]),
+                    dW=grad_err(dtype, grads[mode][1], g * ref["dW"]))
+        print(dtype, mode, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+        assert errs["dh"] <= tol["grad"] and errs["dW"] <= tol["grad"], errs
+        assert np.all(grads[mode][0][inp.mask == 0] == 0.0)
+    assert grad_err(dtype, grads["fused"][0], grads["recompute"][0]) <= tol["grad"]
+    assert grad_err(dtype, grads["fused"][1], grads["recompute"][1]) <= tol["grad"]
+
+
+def test_fused_autograd_mode_with_unit_gradient_is_the_one_call(torch_cuda):
+    """With g = 1 the backward's product is exact: dh (rounded once from the same float32
+    sums) equals the one-call kd_chunked_kl_fwd_bwd output bit for bit, and W's gradient
+    is that call's float32 dW as autograd casts it to W's dtype."""
+    import output_head_kl_amd as kd
+    torch = torch_cuda
+    inp = synth.make(1, seed=30, N=700, d=264, V=3001, K=7, chunk=300, dtype="bf16")
+    inp.mask[[4, 300]] = 0
+    h, W, idx, p, mask = to_device(inp, torch)
+    loss1, dh1, dW1 = kd.fwd_bwd(h, W, idx, p, mask, chunk=300)
+    hg = h.clone().requires_grad_(True)
+    Wg = W.clone().requires_grad_(True)
+    loss = kd.chunked_kl_loss(hg, Wg, idx, p, mask, chunk=300)
+    loss.backward()
+    torch.cuda.synchronize()
+    assert float(loss) == float(loss1[0])
+    assert np.array_equal(_bits(hg.grad, torch), _bits(dh1, torch))
+    assert np.array_equal(_bits(Wg.grad, torch), _bits(dW1.to(torch.bfloat16), torch))
+
+
+def test_scale_grads_rounds_once(torch_cuda):
+    """kd_scale_grads: dh = g * dh_f32 rounded once to bf16 (compared with torch's own
+    float32 product and bf16 rounding), dW scaled in place, and a dW left untouched for
+    g = 1."""
+    import output_head_kl_amd as kd
+    torch = torch_cuda
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dh32 = torch.randn((37, 24), device="cuda", generator=gen)
+    dW = torch.randn((19, 24), device="cuda", generator=gen)
+    dW0 = dW.clone()
+    g = torch.tensor([-0.3], device="cuda")
+    dh, dW_out = kd.scale_grads(g, dh32, dW, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert dW_out.data_ptr() == dW.data_ptr()
+    assert torch.equal(dh, (dh32 * g).to(torch.bfloat16))
+    assert torch.equal(dW, dW0 * g)
+    one = torch.ones(1, device="cuda")
+    dh, _ = kd.scale_grads(one, dh32, dW, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(dh, dh32) and torch.equal(dW, dW0 * g)
