@@ -303,6 +303,26 @@ int kd_teacher_topk(const void *logits, int32_t dtype, int64_t N, int64_t V, int
                     int32_t *topk_idx, float *topk_p, float *row_lse,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kd_teacher_topk_noalloc -- kd_teacher_topk for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument and no allocation of any kind.
+ *
+ * The 256-byte workspace of kd_teacher_topk (one validity flag) is replaced by a
+ * static module array of 256 bytes that every device the library runs on holds from
+ * module load until the process ends.  Its address on the current device is looked up
+ * once per device (hipGetSymbolAddress) on that device's first call; the flag is
+ * cleared by a fill kernel at the start of every call.  Every size the allocating
+ * call accepts fits, so no size is rejected for the scratch; arguments, outputs,
+ * results (bit for bit), limits, stream behaviour and errors are kd_teacher_topk's.
+ * The current device must be the one that logits, the outputs and stream belong to.
+ * All calls on one device share its array: calls that overlap on one device (other
+ * threads, other streams) race on the flag, so they must be serialised by the caller.
+ */
+int kd_teacher_topk_noalloc(const void *logits, int32_t dtype, int64_t N, int64_t V,
+                            int32_t K, int32_t *topk_idx, float *topk_p, float *row_lse,
+                            void *stream);
+
 /* Text describing the last non-OK return on the calling thread ("" if none). */
 const char *kd_last_error(void);
 

@@ -78,6 +78,8 @@ def _lib():
     lib.kd_topk_workspace_bytes.restype = ctypes.c_int
     lib.kd_teacher_topk.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, sz, vp]
     lib.kd_teacher_topk.restype = ctypes.c_int
+    lib.kd_teacher_topk_noalloc.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp]
+    lib.kd_teacher_topk_noalloc.restype = ctypes.c_int
     lib.kd_last_error.argtypes = []
     lib.kd_last_error.restype = ctypes.c_char_p
     lib.kd_version.restype = ctypes.c_int

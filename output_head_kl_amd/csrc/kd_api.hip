@@ -548,14 +548,16 @@ int kd_vocab_shard_combine(const float *shard_max, const float *shard_sumexp,
 int kd_topk_workspace_bytes(size_t *bytes_out) {
   g_err[0] = 0;
   if (!bytes_out) return fail(KD_E_ARG, "bytes_out is NULL");
-  *bytes_out = 256;
+  *bytes_out = kd::kTopkScratchBytes;
   return KD_OK;
 }
 
-int kd_teacher_topk(const void *logits, int32_t dtype, int64_t N, int64_t V, int32_t K,
-                    int32_t *topk_idx, float *topk_p, float *row_lse, void *workspace,
-                    size_t workspace_bytes, void *stream_v) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+int topk_check(const void *logits, int32_t dtype, int64_t N, int64_t V, int32_t K,
+               int32_t *topk_idx, float *topk_p, float *row_lse) {
   if (dtype != KD_F32 && dtype != KD_BF16) return fail(KD_E_ARG, "dtype %d unknown", dtype);
   if (N < 0 || V < 1 || K < 1) return fail(KD_E_ARG, "need N >= 0, V >= 1, K >= 1");
   if (K > V) return fail(KD_E_ARG, "K = %d exceeds V = %lld", K, (long long)V);
@@ -563,17 +565,18 @@ int kd_teacher_topk(const void *logits, int32_t dtype, int64_t N, int64_t V, int
   if (V >= ((int64_t)1 << 29) || N >= ((int64_t)1 << 31))
     return fail(KD_E_UNSUPPORTED, "V must be below 2^29 and N below 2^31");
   if (N > 0 && (!logits || !topk_idx || !topk_p)) return fail(KD_E_ARG, "logits, topk_idx and topk_p are required");
-  if (!workspace) return fail(KD_E_ARG, "workspace is required");
   const size_t es = dtype == KD_BF16 ? 2 : 4;
   if (logits && (uintptr_t)logits % es) return fail(KD_E_ARG, "logits misaligned");
   if (((uintptr_t)topk_idx | (uintptr_t)topk_p | (uintptr_t)row_lse) % 4)
     return fail(KD_E_ARG, "outputs must be 4-byte aligned");
-  if ((uintptr_t)workspace % 256) return fail(KD_E_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < 256) return fail(KD_E_WORKSPACE, "workspace has %zu bytes, needs 256", workspace_bytes);
-  if (N == 0) return KD_OK;
-  hipStream_t stream = (hipStream_t)stream_v;
-  int *flags = (int *)workspace;
-  LAUNCH(kd::KC_MISC, kd::launch_fill_zero(flags, 64, stream));
+  return KD_OK;
+}
+
+// The validity flag at `flags` is cleared by a fill kernel, raised by the producer for a
+// bad row, and read back after one stream synchronisation.
+int topk_run(const void *logits, int32_t dtype, int64_t N, int64_t V, int32_t K,
+             int32_t *topk_idx, float *topk_p, float *row_lse, int *flags, hipStream_t stream) {
+  LAUNCH(kd::KC_MISC, kd::launch_fill_zero(flags, sizeof(int), stream));
   LAUNCH(kd::KC_TOPK, kd::launch_teacher_topk(dtype, logits, N, V, K, topk_idx, topk_p, row_lse,
                                               flags, stream));
   int hf = 0;
@@ -581,6 +584,38 @@ int kd_teacher_topk(const void *logits, int32_t dtype, int64_t N, int64_t V, int
   HIPCHK(hipStreamSynchronize(stream));
   if (hf) return fail(KD_E_INDEX, "a row has a NaN or +inf logit or no finite logit; outputs undefined");
   return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_teacher_topk(const void *logits, int32_t dtype, int64_t N, int64_t V, int32_t K,
+                    int32_t *topk_idx, float *topk_p, float *row_lse, void *workspace,
+                    size_t workspace_bytes, void *stream_v) {
+  g_err[0] = 0;
+  int rc = topk_check(logits, dtype, N, V, K, topk_idx, topk_p, row_lse);
+  if (rc != KD_OK) return rc;
+  if (!workspace) return fail(KD_E_ARG, "workspace is required");
+  if ((uintptr_t)workspace % 256) return fail(KD_E_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < kd::kTopkScratchBytes)
+    return fail(KD_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                kd::kTopkScratchBytes);
+  if (N == 0) return KD_OK;
+  return topk_run(logits, dtype, N, V, K, topk_idx, topk_p, row_lse, (int *)workspace,
+                  (hipStream_t)stream_v);
+}
+
+int kd_teacher_topk_noalloc(const void *logits, int32_t dtype, int64_t N, int64_t V, int32_t K,
+                            int32_t *topk_idx, float *topk_p, float *row_lse, void *stream_v) {
+  g_err[0] = 0;
+  int rc = topk_check(logits, dtype, N, V, K, topk_idx, topk_p, row_lse);
+  if (rc != KD_OK) return rc;
+  if (N == 0) return KD_OK;
+  int *flags = nullptr;
+  HIPCHK(kd::topk_scratch(&flags));
+  return topk_run(logits, dtype, N, V, K, topk_idx, topk_p, row_lse, flags,
+                  (hipStream_t)stream_v);
 }
 
 int kd_profile_enable(int on) {

@@ -152,6 +152,12 @@ hipError_t launch_shard_combine(const float *m, const float *sx, const float *pz
 
 // --- teacher top-K cache producer (kd_topk.hip) ---
 constexpr int kTopkMaxK = 256;
+// Workspace of kd_teacher_topk, and the size of the module scratch that replaces it in
+// kd_teacher_topk_noalloc: one validity flag (int), padded to 256 bytes.
+constexpr size_t kTopkScratchBytes = 256;
+// The current device's copy of the module scratch (kTopkScratchBytes), looked up once per
+// device with hipGetSymbolAddress; allocates nothing.
+hipError_t topk_scratch(int **out);
 // One workgroup per row; flags[0] |= 1 for a row with a NaN or +inf logit or with no
 // finite logit.  lse may be null.
 hipError_t launch_teacher_topk(int dtype, const void *logits, int64_t N, int64_t V, int32_t K,

@@ -22,8 +22,40 @@
 #include "kd_internal.h"
 
 #include <cstdint>
+#include <mutex>
 
 namespace kd {
+
+// Scratch of the allocation-free entry point (kd_teacher_topk_noalloc): the validity flag
+// the kernel raises, in module memory that exists on every device the library runs on
+// from module load until the process ends.  Host code never passes `scratch` itself (on
+// the host it names a stand-in, not the device copy): topk_scratch() looks up each
+// device's address once and every launch takes that.
+static __device__ __align__(256) int scratch[kTopkScratchBytes / sizeof(int)];
+static_assert(sizeof(int) <= kTopkScratchBytes, "the flag fits the scratch");
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t topk_scratch(int **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (int *)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 namespace {
 
