@@ -475,7 +475,7 @@ struct EpiFwdLse {
     __builtin_amdgcn_sched_barrier(0);
     // (max, sum exp) per wave row and token, and u
     const int vl = m0 + (lane >> 5) * 4;
-    if constexpr (DT == 1 && NRB % 3 == 0) {
+    if constexpr (DT == 1 && NRB % 2 == 0 && NRB >= 4) {
       staged_u(acc, m0, n0, lane, smem);
       return;
     }
@@ -546,16 +546,18 @@ struct EpiFwdLse {
   }
 
   // bf16, 192-row waves: as above, but u (when wanted) goes out through LDS so that the
-  // stores are whole 16-byte pieces of a token's vocabulary run (192 contiguous bytes
-  // per token and pass) instead of 8-byte pieces for 32 tokens at once.  They are
-  // non-temporal: u is streamed once into the rescale, and the GEMM's operands keep L2.  Each wave
-  // stages its own 96 rows x 32*NCB tokens per pass in a private slice of LDS (13 KB);
-  // the workgroup barrier first lets every wave finish with the gather's staging buffer.
+  // stores are whole 16-byte pieces of a token's vocabulary run instead of 8-byte pieces
+  // for 32 tokens at once.  A pass covers 64 rows, so each token's run is one aligned
+  // 128-byte line (wave rows start at multiples of 192 rows, three lines) and no line is
+  // written in parts by two passes.  The stores are non-temporal: u is streamed once into
+  // the rescale, and the GEMM's operands keep L2.  Each wave stages its own 64 rows x
+  // 32*NCB tokens per pass in a private slice of LDS (9 KB); the workgroup barrier first
+  // lets every wave finish with the gather's staging buffer.
   template <int NRB, int NCB>
   __device__ __forceinline__ void staged_u(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
                                            char *smem) const {
-    constexpr int WR = 32 * NRB, RP = 3, NP = NRB / RP;  // 32-row blocks per pass, passes
-    constexpr int TOK = 32 * NCB, PITCH = 104;            // tokens per wave, bf16 per row
+    constexpr int WR = 32 * NRB, RP = 2, NP = NRB / RP;  // 32-row blocks per pass, passes
+    constexpr int TOK = 32 * NCB, PITCH = RP * 32 + 8;    // tokens per wave, bf16 per row
     constexpr int QPR = RP * 32 / 8;                      // 16-byte pieces per token row
     const bool keep = u != nullptr;                       // the same for the workgroup
     if (keep) __syncthreads();
@@ -649,7 +651,7 @@ struct EpiBwdDz {
   template <int NRB, int NCB>
   __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
                                              int, char *smem) const {
-    if constexpr (DT == 1 && NRB % 3 == 0) {
+    if constexpr (DT == 1 && NRB % 2 == 0 && NRB >= 4) {
       staged(acc, m0, n0, lane, smem);
       return;
     }
@@ -698,15 +700,16 @@ struct EpiBwdDz {
     }
   }
 
-  // bf16, 192-row waves: dz and dzT leave through a per-wave LDS slice ([64 tokens][96
-  // rows] per pass, 13 KB), dz as 16-byte pieces of each token's 96-row run, dzT as
-  // 16-byte pieces (8 tokens) of each row's 64-token run, instead of 8-byte and 4-byte
-  // scattered stores.  dzT is read only by the group's dW GEMM: non-temporal stores.
+  // bf16, 192-row waves: dz and dzT leave through a per-wave LDS slice ([64 tokens][64
+  // rows] per pass, 9 KB), dz as 16-byte pieces of each token's 64-row run (one aligned
+  // 128-byte line), dzT as 16-byte pieces (8 tokens) of each row's 64-token run, instead
+  // of 8-byte and 4-byte scattered stores.  dzT is read only by the group's dW GEMM:
+  // non-temporal stores.
   template <int NRB, int NCB>
   __device__ __forceinline__ void staged(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
                                          char *smem) const {
-    constexpr int RP = 3, NP = NRB / RP;                 // 32-row blocks per pass, passes
-    constexpr int TOK = 32 * NCB, PITCH = 104;           // tokens per wave, bf16 per row
+    constexpr int RP = 2, NP = NRB / RP;                 // 32-row blocks per pass, passes
+    constexpr int TOK = 32 * NCB, PITCH = RP * 32 + 8;   // tokens per wave, bf16 per row
     constexpr int QPR = RP * 32 / 8;                     // 16-byte pieces per token row
     constexpr int TG = TOK / 8;                          // 8-token groups per vocabulary row
     __syncthreads();  // every wave is done with the k-loop's LDS ring
