@@ -42,18 +42,32 @@ def warm_up(step, n, seconds=0.5):
     return k
 
 
+def timed_steps(step, steps):
+    """`steps` calls of step, each bracketed by device synchronisations: (list of ms per
+    call, the last call's output).  The previous call's outputs go back to the pool before
+    the next call, so peak memory is that of one call."""
+    import torch
+    out = None
+    times = []
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        out = None
+        t0 = time.perf_counter()
+        out = step()
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t0) * 1e3)
+    return times, out
+
+
 def timed_then_profiled(step, steps):
-    """Time `steps` calls of step with nothing else recorded, then run them again with
-    the library's per-launch HIP events on: (ms per call, kernel table of that pass)."""
+    """Time `steps` calls of step with nothing else recorded (median of the calls), then
+    run them again with the library's per-launch HIP events on: (ms per call, kernel table
+    of that pass)."""
     import torch
 
     import output_head_kl_amd as kd
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / steps * 1e3
+    times, _ = timed_steps(step, steps)
+    ms = float(np.median(times))
     kd.profile_read()
     kd.profile_enable(True)
     for _ in range(steps):
@@ -85,19 +99,27 @@ def parse():
                     help="time one GPU's share of a vocabulary-sharded head: rows [0, V/G) of W "
                          "with the full token batch (forward statistics + backward); G = value")
     ap.add_argument("--torch-baselines", action="store_true",
-                    help="context only: peak memory and time of a dense and a forward-chunked "
-                         "PyTorch implementation of the same loss (torch autograd, hipBLASLt "
-                         "GEMMs) next to the fused library call, N = 4K..128K; prints one JSON line")
+                    help="context only: peak memory, time and loss of a dense and a "
+                         "forward-chunked PyTorch implementation of the same loss (torch "
+                         "autograd, hipBLASLt GEMMs) next to the fused library call, "
+                         "N = 4K..256K; prints one JSON line")
     ap.add_argument("--topk", action="store_true",
                     help="time the teacher top-K cache producer (kd_teacher_topk) on N=32768 rows "
                          "of V=128256 bf16 teacher logits, K=100; prints one JSON line")
     ap.add_argument("--memory-sweep", action="store_true",
-                    help="measure peak device memory of one call for N = 4K .. 256K tokens "
-                         "(d=3072, V=128256, K=100, chunk 4096) and fit a + b*N; prints one "
-                         "JSON line and exits")
+                    help="measure peak device memory of one call and the steady time per call "
+                         "for N = 4K .. 256K tokens (d=3072, V=128256, K=100, chunk 4096) and "
+                         "fit peak = a + b*N; prints one JSON line and exits")
     ap.add_argument("--dw-group-tokens", type=int, default=None,
                     help="allocate the workspace for dW groups of at most this many tokens "
                          "(0 = one chunk, the smallest workspace); default 16384")
+    ap.add_argument("--no-small-workspace", action="store_true",
+                    help="skip the second measurement with the smallest workspace (dW "
+                         "accumulated one chunk at a time: no buffer beyond one chunk of logits)")
+    ap.add_argument("--autograd", action="store_true",
+                    help="time the loss as a torch autograd function (chunked_kl_loss forward + "
+                         "backward), in its fused mode and in its recompute mode; prints one "
+                         "JSON line")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="after the run, launch one plain device copy of this many GiB "
                          "(a kernel of known traffic, for scaling HBM byte counters)")
@@ -226,8 +248,12 @@ def bench_topk(args):
 
 def torch_baselines():
     """The loss written with torch ops, as a dense and as a forward-chunked autograd graph,
-    for the pages' memory comparison (output head only).  Not part of the library: these
-    run torch's kernels; the library's own call is timed beside them."""
+    for the pages' memory comparison (output head only), beside the fused library call, for
+    N = 4K .. 256K tokens.  Per N and implementation: peak device memory of one call
+    (forward and backward), the steady time per call, and the loss, which must equal the
+    library's (each graph computes the same mean loss on the same inputs; the torch graphs
+    round the logits to bf16 in their matrix product, the library keeps them in fp32).  Not
+    part of the library: these run torch's kernels."""
     import torch
 
     import output_head_kl_amd as kd
@@ -242,45 +268,68 @@ def torch_baselines():
         return (ell * mask).sum() / count
 
     results = []
-    for N in [4096, 16384, 32768, 65536, 131072]:
+    for N in [4096, 16384, 32768, 65536, 131072, 262144]:
         h0 = torch.randn(N, d, device="cuda", generator=g, dtype=torch.bfloat16)
         idx = torch.randint(0, V, (N, K), device="cuda", generator=g, dtype=torch.int32)
         p = torch.rand(N, K, device="cuda", generator=g) / K
         mask = torch.ones(N, device="cuda")
         row = {"N": N}
-        for kind in ["dense", "forward_chunked", "fused_library"]:
+        for kind in ["fused_library", "forward_chunked", "dense"]:
+            def call():
+                if kind == "fused_library":
+                    out = kd.fwd_bwd(h0, W0, idx, p, mask.to(torch.uint8), chunk=chunk)
+                    return float(out[0].item())
+                h = h0.detach().requires_grad_(True)
+                W = W0.detach().requires_grad_(True)
+                if kind == "dense":
+                    loss = loss_of(h, W, idx, p, mask, float(N))
+                else:  # chunks in the forward; autograd keeps every chunk's logits
+                    loss = sum(loss_of(h[c:c + chunk], W, idx[c:c + chunk], p[c:c + chunk],
+                                       mask[c:c + chunk], float(N))
+                               for c in range(0, N, chunk))
+                loss.backward()
+                val = float(loss.detach().item())
+                del loss, h, W
+                return val
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
             torch.cuda.reset_peak_memory_stats()
             try:
                 t0 = time.perf_counter()
-                if kind == "fused_library":
-                    out = kd.fwd_bwd(h0, W0, idx, p, mask.to(torch.uint8), chunk=chunk)
-                    del out
-                else:
-                    h = h0.detach().requires_grad_(True)
-                    W = W0.detach().requires_grad_(True)
-                    if kind == "dense":
-                        loss = loss_of(h, W, idx, p, mask, float(N))
-                    else:  # chunks in the forward; autograd keeps every chunk's logits
-                        loss = sum(loss_of(h[c:c + chunk], W, idx[c:c + chunk], p[c:c + chunk],
-                                           mask[c:c + chunk], float(N))
-                                   for c in range(0, N, chunk))
-                    loss.backward()
-                    del loss, h, W
+                loss_val = call()          # first call: peak memory (and warm-up)
                 torch.cuda.synchronize()
-                row[kind] = {"peak_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
-                             "s": round(time.perf_counter() - t0, 3)}
+                first_s = time.perf_counter() - t0
+                peak = torch.cuda.max_memory_allocated()
+                reps = 3 if first_s < 2.0 else 1
+                times = []
+                for _ in range(reps):     # steady time per call
+                    t0 = time.perf_counter()
+                    call()
+                    torch.cuda.synchronize()
+                    times.append(time.perf_counter() - t0)
+                row[kind] = {"peak_gib": round(peak / 2**30, 3),
+                             "s_per_call": round(float(np.median(times)), 4),
+                             "tokens_per_s": round(N / float(np.median(times)), 1),
+                             "loss": loss_val}
             except torch.cuda.OutOfMemoryError:
                 row[kind] = "out of memory"
             torch.cuda.empty_cache()
             print(f"[baselines] N={N} {kind}: {row[kind]}", file=sys.stderr, flush=True)
+        ref = row["fused_library"]["loss"] if isinstance(row.get("fused_library"), dict) else None
+        for kind in ["forward_chunked", "dense"]:
+            if isinstance(row.get(kind), dict) and ref is not None:
+                row[kind]["loss_rel_diff_vs_library"] = abs(row[kind]["loss"] - ref) / abs(ref)
         results.append(row)
         del h0, idx, p, mask
+    bad = [(r["N"], k, r[k]["loss_rel_diff_vs_library"]) for r in results
+           for k in ("forward_chunked", "dense")
+           if isinstance(r.get(k), dict) and r[k]["loss_rel_diff_vs_library"] > 2e-3]
     print(json.dumps({"torch_baselines": {"d": d, "V": V, "K": K, "chunk": chunk, "dtype": "bf16",
-                                          "note": "one call each (first call includes "
-                                                  "library and kernel warm-up)",
+                                          "loss_check": "every torch loss within 2e-3 of the "
+                                                        "library's" if not bad else f"FAILED {bad}",
                                           "rows": results}}), flush=True)
+    if bad:
+        sys.exit(1)
 
 
 def memory_sweep(dw_group_tokens=None):
@@ -320,15 +369,23 @@ def memory_sweep(dw_group_tokens=None):
         res1 = torch.cuda.memory_reserved()
         peaks.append(torch.cuda.max_memory_allocated())
         largest = max(ws_bytes, N * d * 2, V * d * 4)   # workspace, dh, dW
+        # iteration rate: steady time per call (the call above warmed up), workspace reused
+        del out
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        step = lambda: kd.fwd_bwd(h, W, idx, p, mask, chunk=chunk, workspace=ws)
+        warm_up(step, 1, seconds=0.3)
+        times, out = timed_steps(step, 3)
+        ms = float(np.median(times))
         rows.append({"N": N, "peak_bytes": peaks[-1], "workspace_bytes": ws_bytes,
                      "device_free_drop_bytes": free0 - free1,
                      "torch_reserved_growth_bytes": res1 - res0,
                      "largest_allocation_bytes": largest,
-                     "dense_bf16_logits_bytes": N * V * 2})
-        del h, idx, p, mask, out
+                     "dense_bf16_logits_bytes": N * V * 2,
+                     "ms_per_call": round(ms, 3), "tokens_per_s": round(N / (ms * 1e-3), 1)})
+        del h, idx, p, mask, out, ws
         print(f"[memory] N={N}: peak {peaks[-1] / 2**30:.3f} GiB, free drop "
-              f"{(free0 - free1) / 2**20:.1f} MiB, reserved growth {(res1 - res0) / 2**20:.1f} MiB",
-              file=sys.stderr, flush=True)
+              f"{(free0 - free1) / 2**20:.1f} MiB, reserved growth {(res1 - res0) / 2**20:.1f} MiB, "
+              f"{ms:.2f} ms per call", file=sys.stderr, flush=True)
     def linfit(x, y):
         b, a = np.polyfit(x, y, 1)
         fit = a + b * x
@@ -405,6 +462,49 @@ def bench_split(args, kd, torch, cfg, h, W, idx, p, mask, ws):
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
         "kernels_fwd": fk, "kernels_bwd": bk, "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_autograd(args, kd, torch, cfg, h, W, idx, p, mask):
+    """The loss as a torch autograd function of h and W: forward and backward of
+    chunked_kl_loss, in its fused mode (one-call loss and gradients held for the backward)
+    and in its recompute mode (the backward recomputes the logits)."""
+    hg = h.detach().clone().requires_grad_(True)
+    Wg = W.detach().clone().requires_grad_(True)
+    res_modes = {}
+    for mode in ("fused", "recompute"):
+        def step():
+            hg.grad = None
+            Wg.grad = None
+            loss = kd.chunked_kl_loss(hg, Wg, idx, p, mask, chunk=cfg.chunk, mode=mode)
+            loss.backward()
+            return loss.detach()
+
+        warm_up(step, args.warmup)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        times, loss = timed_steps(step, args.steps)
+        ms = float(np.median(times))
+        res_modes[mode] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(cfg.N / (ms * 1e-3), 1),
+                           "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
+                           "loss": float(loss)}
+        print(f"[bench] autograd {mode}: {ms:.2f} ms per step", file=sys.stderr, flush=True)
+    ms = res_modes["fused"]["ms_per_step"]
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    workload = f"fused_kl_autograd_N{cfg.N}_d{cfg.d}_V{cfg.V}_K{cfg.K}_chunk{cfg.chunk}_{cfg.dtype}"
+    res = {
+        "metric": "tokens/s, fused KL as a torch autograd function (chunked_kl_loss forward + "
+                  "backward, fused mode), N=32K d=3072 V=128256 K=100",
+        "value": res_modes["fused"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload, "N": cfg.N, "d": cfg.d, "V": cfg.V, "K": cfg.K,
+                   "chunk": cfg.chunk, "mask": cfg.mask},
+        "tflops_executed_6NVd": round(6.0 * cfg.N * cfg.V * cfg.d / (ms * 1e-3) / 1e12, 1),
+        "frac_of_peak_executed": round(6.0 * cfg.N * cfg.V * cfg.d / (ms * 1e-3) / 1e12 / peak, 4),
+        "modes": res_modes, "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
 
@@ -506,6 +606,9 @@ def main():
 
     if args.split:
         return bench_split(args, kd, torch, cfg, h, W, idx, p, mask, ws)
+    if args.autograd:
+        del ws
+        return bench_autograd(args, kd, torch, cfg, h, W, idx, p, mask)
     if args.shard:
         return bench_shard(args, kd, torch, cfg, h, W, idx, p, mask)
 
@@ -513,14 +616,7 @@ def main():
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
     prof = not args.no_profile
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    out = None
-    for _ in range(args.steps):
-        out = None       # the previous step's outputs go back to the pool first, so the
-        out = step()     # peak below is that of one call
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    step_ms, out = timed_steps(step, args.steps)
     loss_val = float(out[0].item())
     del out
     ms_profiled = None
@@ -542,8 +638,8 @@ def main():
         del out
     peak_gib = torch.cuda.max_memory_allocated() / 2**30
 
-    ms = elapsed / args.steps * 1e3
-    tokens_per_s = cfg.N * args.steps / elapsed
+    ms = float(np.median(step_ms))
+    tokens_per_s = cfg.N / (ms * 1e-3)
     # the fused call runs three GEMMs per chunk (z, dh, dW): its backward takes dz from the
     # forward's exp(z - max) instead of recomputing z, so 6NVd flops are executed; 8NVd is
     # the work of the recompute formulation (the split fwd/bwd entry points), for context
@@ -581,6 +677,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "ms_per_step_mean": round(float(np.mean(step_ms)), 3),
+        "ms_per_step_all": [round(x, 3) for x in step_ms],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -600,6 +698,29 @@ def main():
         "ms_per_step_profiled_pass": None if ms_profiled is None else round(ms_profiled, 3),
         "cpu_baseline": None,
     }
+    if args.dw_group_tokens is None and not args.no_small_workspace and cfg.dtype == "bf16":
+        # the same workload with the smallest workspace the call accepts: dW is accumulated
+        # chunk by chunk, so no buffer holds more than one chunk of logits
+        del ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        ws0 = torch.empty(kd.workspace_bytes(cfg.N, cfg.d, cfg.V, cfg.K, cfg.chunk, dt_code, 0),
+                          dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+
+        def step0():
+            return kd.fwd_bwd(h, W, idx, p, mask, chunk=cfg.chunk, workspace=ws0)
+
+        warm_up(step0, 1)
+        t0_ms, out0 = timed_steps(step0, args.steps)
+        res["smallest_workspace"] = {
+            "dw_group_tokens": 0, "workspace_bytes": ws0.numel(),
+            "ms_per_step": round(float(np.median(t0_ms)), 3),
+            "tokens_per_s": round(cfg.N / (float(np.median(t0_ms)) * 1e-3), 1),
+            "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
+            "loss": float(out0[0].item())}
+        del out0, ws0
     if args.copy_gib > 0:
         n = int(args.copy_gib * 2**30) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
