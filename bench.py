@@ -669,8 +669,11 @@ def main():
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                         "traffic": traffic_for(dom, workload)}
 
+    headline = (cfg.N, cfg.d, cfg.V, cfg.K) == (32768, 3072, 128256, 100)
     res = {
-        "metric": "tokens/s + MFMA util, fused KL fwd+bwd, N=32K d=3072 V=128256 K=100",
+        "metric": ("tokens/s + MFMA util, fused KL fwd+bwd, N=32K d=3072 V=128256 K=100"
+                   if headline else f"tokens/s + MFMA util, fused KL fwd+bwd, N={cfg.N} "
+                                    f"d={cfg.d} V={cfg.V} K={cfg.K}"),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
