@@ -68,8 +68,12 @@ def timed_then_profiled(step, steps):
     import output_head_kl_amd as kd
     times, _ = timed_steps(step, steps)
     ms = float(np.median(times))
+    # recorded steps first, discarded, for at least 0.5 s: they fill the library's pool
+    # of HIP events and bring the GPU back to its steady clock under the recording
     kd.profile_read()
     kd.profile_enable(True)
+    warm_up(step, 1)
+    kd.profile_read()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
@@ -622,11 +626,13 @@ def main():
     ms_profiled = None
     if prof:
         # Per-kernel times: the same K steps again with HIP events recorded on the
-        # library's stream around every launch.  The event records cost ~1 ms per step,
-        # so they stay out of the pass that gives `value`.
+        # library's stream around every launch (after recorded steps for at least 0.5 s,
+        # discarded).  The records cost ~1 ms per step, so they stay out of the pass that
+        # gives `value`.
         kd.profile_read()          # discard anything recorded so far
         kd.profile_enable(True)
-        torch.cuda.synchronize()
+        warm_up(step, 1)           # recorded and discarded (event pool, steady clock)
+        kd.profile_read()
         tp = time.perf_counter()
         for _ in range(args.steps):
             out = None

@@ -39,6 +39,19 @@ struct Prof {
   bool on = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[kd::KC_COUNT];
   hipEvent_t pending[kd::KC_COUNT] = {};
+  // Events are reused rather than created per launch: creating two per launch kept the
+  // host busy between launches and let the GPU idle (the profiled pass ran slower).
+  std::vector<hipEvent_t> spare;
+  hipEvent_t take() {
+    hipEvent_t e = nullptr;
+    if (!spare.empty()) {
+      e = spare.back();
+      spare.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+    }
+    return e;
+  }
 };
 Prof g_prof;
 std::mutex g_prof_mu;
@@ -91,16 +104,16 @@ namespace kd {
 
 void prof_begin(int cls, hipStream_t s) {
   if (!g_prof.on) return;
-  hipEvent_t a;
-  if (hipEventCreate(&a) != hipSuccess) return;
+  hipEvent_t a = g_prof.take();
+  if (!a) return;
   (void)hipEventRecord(a, s);
   g_prof.pending[cls] = a;
 }
 
 void prof_end(int cls, hipStream_t s) {
   if (!g_prof.on || !g_prof.pending[cls]) return;
-  hipEvent_t b;
-  if (hipEventCreate(&b) != hipSuccess) return;
+  hipEvent_t b = g_prof.take();
+  if (!b) return;
   (void)hipEventRecord(b, s);
   g_prof.ev[cls].emplace_back(g_prof.pending[cls], b);
   g_prof.pending[cls] = nullptr;
@@ -643,8 +656,8 @@ int kd_profile_read(int cls, double *total_ms, int64_t *launches) {
       tot += ms;
       ++n;
     }
-    (void)hipEventDestroy(pr.first);
-    (void)hipEventDestroy(pr.second);
+    g_prof.spare.push_back(pr.first);
+    g_prof.spare.push_back(pr.second);
   }
   g_prof.ev[cls].clear();
   *total_ms = tot;

@@ -121,6 +121,8 @@ struct GemmGrid {
   int k_len;    // k range of one split (multiple of the k-step)
   int k_total;  // loop bound
   int order;    // 0: n-tile index fastest, 1: m-tile index fastest
+  int ngrp;     // order 0 (bf16 pipe kernel): n tiles taken in groups of ngrp, all m
+                // tiles of a group before the next group (0: one group)
 };
 
 template <int DT> struct Elem;
@@ -1065,8 +1067,15 @@ void gemm_pipe_kernel(Operand A, Operand B, GemmGrid G, Epi epi) {
   const int rem = lin - split * per_split;
   int tm, tn;
   if (G.order == 0) {
-    tm = rem / G.ntn;
-    tn = rem - tm * G.ntn;
+    if (G.ngrp > 0 && G.ngrp < G.ntn) {
+      const int span = G.ntm * G.ngrp, grp = rem / span;
+      const int gs = min(G.ngrp, G.ntn - grp * G.ngrp), r = rem - grp * span;
+      tm = r / gs;
+      tn = grp * G.ngrp + (r - tm * gs);
+    } else {
+      tm = rem / G.ntn;
+      tn = rem - tm * G.ntn;
+    }
   } else {
     tn = rem / G.ntm;
     tm = rem - tn * G.ntm;
@@ -1237,7 +1246,10 @@ hipError_t launch_fwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
   // vocabulary tiles cover V_pad (a multiple of the tile), so u is written for every row
   Operand A{W, d, (int)V, (int)d, 256};
   Operand B{h_c, d, (int)rows, (int)d, 256};
-  GemmGrid G{(int)(V_pad / tile_rows(dtype)), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
+  // Eight token tiles per raster group: an XCD's 32 concurrent workgroups then cover
+  // four vocabulary tiles x eight token tiles, the fewest distinct operand rows per stage
+  // (more token tiles per chunk would otherwise spread them over two vocabulary tiles).
+  GemmGrid G{(int)(V_pad / tile_rows(dtype)), cdiv(rows, kTile), 1, (int)d, (int)d, 0, 8};
   if (dtype == 1) {
     EpiFwdLse<1> e{partials, ld_part, (int)V, (int)rows, boff, bent, G.ntn, zg, (int)K, u,
                    C_alloc * 256, (int)V_pad};
@@ -1374,7 +1386,7 @@ hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
                            int64_t tst, int64_t V_pad, int64_t C_alloc, hipStream_t s) {
   Operand A{W, d, (int)V, (int)d, 256};
   Operand B{h_c, d, (int)rows, (int)d, 256};
-  GemmGrid G{(int)(V_pad / tile_rows(dtype)), cdiv(rows, kTile), 1, (int)d, (int)d, 0};
+  GemmGrid G{(int)(V_pad / tile_rows(dtype)), cdiv(rows, kTile), 1, (int)d, (int)d, 0, 8};
   if (dtype == 1) {
     EpiBwdDz<1> e{dz, C_alloc * 256, lse, sM, (int)V, (int)rows, (int)V_pad,
                   (unsigned short *)dzt, tst};
