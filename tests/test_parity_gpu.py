@@ -59,6 +59,22 @@ def test_ragged_shapes_in_full(torch_cuda, dtype):
     _check_full(inp, run(inp, torch_cuda))
 
 
+def test_token_tile_groups_with_a_partial_group(torch_cuda):
+    """A chunk of eleven 256-token tiles: the logits GEMMs take token tiles in groups of
+    eight, so the chunk has one whole group and a partial one of three (with a partial
+    last token tile), over several vocabulary tiles; in full against the oracle, for the
+    one call and for the split pair (whose recompute GEMM takes the same order)."""
+    inp = synth.make(1, seed=81, N=2700, d=128, V=2500, K=9, chunk=2700)
+    inp.mask[[1, 2048, 2699]] = 0
+    got = run(inp, torch_cuda)
+    ref = _check_full(inp, got)
+    split = _run_split(inp, torch_cuda)
+    tol = TOL["bf16"]
+    assert rel(split["loss"][0], ref["loss"]) <= tol["loss"]
+    assert grad_err("bf16", split["dh"], ref["dh"]) <= tol["grad"]
+    assert grad_err("bf16", split["dW"], ref["dW"]) <= tol["grad"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_wide_logit_range(torch_cuda, dtype):
     """Logits with a standard deviation near 60: for most 192-row vocabulary groups of a
