@@ -26,6 +26,64 @@ PEAK_HBM_GBS = 8000.0
 GEMM_CLASSES = ("fwd_gemm_lse", "bwd_gemm_dz", "dh_gemm", "dw_gemm")
 
 
+class ClockSampler:
+    """While active, samples the GPU's current graphics clock and socket power through
+    amd-smi every `period` seconds in a thread; `result()` gives their means over the
+    samples, or None where amd-smi is not available (one GPU visible to it only)."""
+
+    def __init__(self, period=0.005):
+        self.period, self.mhz, self.watts, self._stop = period, [], [], None
+
+    def __enter__(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if len(hs) != 1:
+                amdsmi.amdsmi_shut_down()
+                return self
+        except Exception:  # amd-smi missing or not permitted: no clock figure
+            return self
+        self._smi, self._h = amdsmi, hs[0]
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.mhz.append(float(self._smi.amdsmi_get_clock_info(
+                        self._h, self._smi.AmdSmiClkType.GFX)["clk"]))
+                    self.watts.append(float(self._smi.amdsmi_get_power_info(
+                        self._h)["current_socket_power"]))
+                except Exception:
+                    pass
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._stop is not None:
+            self._stop.set()
+            self._thread.join()
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+        return False
+
+    def result(self):
+        if not self.mhz:
+            return None
+        return {"gfx_mhz_mean": round(float(np.mean(self.mhz)), 1),
+                "gfx_mhz_min": round(float(np.min(self.mhz)), 1),
+                "socket_power_w_mean": round(float(np.mean(self.watts)), 1) if self.watts else None,
+                "samples": len(self.mhz),
+                "source": "amd-smi current graphics clock and socket power, sampled every 5 ms "
+                          "over the timed steps"}
+
+
 def warm_up(step, n, seconds=0.5):
     """At least n untimed calls of step, and calls for at least `seconds` of wall time:
     a few short steps do not bring the GPU to its steady clock."""
@@ -620,7 +678,8 @@ def main():
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
     prof = not args.no_profile
-    step_ms, out = timed_steps(step, args.steps)
+    with ClockSampler() as clk:
+        step_ms, out = timed_steps(step, args.steps)
     loss_val = float(out[0].item())
     del out
     ms_profiled = None
@@ -700,6 +759,11 @@ def main():
         "tflops_executed_6NVd": round(tflops, 1),
         "frac_of_peak_executed": round(tflops / peak, 4),
         "tflops_recompute_equiv_8NVd": round(tflops_recompute_equiv, 1),
+        # the peak assumes 2.4 GHz; against the clock the chip actually ran at
+        "clock_observed": clk.result(),
+        "frac_of_peak_at_observed_clock": (
+            None if clk.result() is None
+            else round(tflops / (peak * clk.result()["gfx_mhz_mean"] / 2400.0), 4)),
         "peak_mem_gib": round(peak_gib, 3),
         "loss": loss_val,
         "roofline": roofline,
