@@ -1,5 +1,6 @@
 """The Python binding rejects tensors that are not on the call's GPU before it touches the
 library (CPU only: the library is replaced by an object that fails on any use)."""
+import os
 import types
 
 import pytest
@@ -71,3 +72,18 @@ def test_unknown_autograd_mode_is_rejected(no_library):
     h, W, idx, p, mask = _inputs("cpu")
     with pytest.raises(ValueError, match="mode"):
         kd.chunked_kl_loss(h, W, idx, p, mask, mode="dense")
+
+
+def test_c_driver_is_built_and_checks_its_input(tmp_path):
+    """The C caller used by the GPU tests is built next to the library and refuses a bad
+    command line or input file before it touches a GPU."""
+    import subprocess
+    drv = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "kd_driver")
+    assert os.path.exists(drv), "build the library first (__graft_entry__.build())"
+    r = subprocess.run([drv], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
+    bad = tmp_path / "bad.bin"
+    bad.write_bytes(b"\0" * 56)
+    r = subprocess.run([drv, str(bad), str(tmp_path / "out.bin")], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 1 and "not a problem file" in r.stderr
