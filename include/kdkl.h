@@ -127,7 +127,10 @@ int kd_workspace_bytes_group(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
  * stream: a hipStream_t (NULL = the null stream).  All work is enqueued on it.
  *   The call synchronises the stream once, after validating the teacher entries
  *   and counting the mask; the rest is asynchronous and the outputs are ready when
- *   the stream's work completes.  Calls sharing one workspace must not overlap.
+ *   the stream's work completes.  Calls sharing one workspace must not overlap;
+ *   calls from different host threads with their own workspaces and outputs may run
+ *   at the same time, on one stream or on several (the library keeps no device state
+ *   between calls, and its host state, the last error, is per thread).
  * Errors: host-side checks run before any device work (KD_E_ARG,
  *   KD_E_UNSUPPORTED, KD_E_WORKSPACE).  Invalid teacher entries give
  *   KD_E_INDEX with no output written.  kd_last_error() describes the failure.
@@ -326,7 +329,7 @@ int kd_teacher_topk_noalloc(const void *logits, int32_t dtype, int64_t N, int64_
 /* Text describing the last non-OK return on the calling thread ("" if none). */
 const char *kd_last_error(void);
 
-/* Library interface version (increments on any change to this header). */
+/* Library interface version: 3 (it increments when a call is added or changes). */
 int kd_version(void);
 
 /*

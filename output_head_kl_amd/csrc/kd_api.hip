@@ -188,7 +188,7 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
 
 extern "C" {
 
-int kd_version(void) { return 2; }
+int kd_version(void) { return 3; }
 
 const char *kd_last_error(void) { return g_err; }
 
