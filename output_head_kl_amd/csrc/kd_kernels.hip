@@ -820,12 +820,15 @@ struct EpiDw {
   struct Pre {};
   float *dW;
   int d, V, accumulate;
+  int lds_rmw;  // accumulate by reading the old values through LDS (bf16 pipe kernel only)
   template <int NRB, int NCB>
   __device__ __forceinline__ void operator()(f32x16 (&acc)[NRB][NCB], int m0, int n0, int lane,
-                                             int, char *) const {
+                                             int, char *smem) const {
     // One buffer resource per wave, from its first row to the end of dW: elements of
     // rows v >= V lie outside its range and the hardware drops them; lanes with
     // j >= d get an offset outside every range.  Offsets stay below 32 * NRB * d * 4 bytes.
+    if (NCB == 2 && NRB % 2 == 0 && accumulate && lds_rmw)
+      __syncthreads();  // (every wave) all have left the k-loop: the operand ring is free
     const long long rem = (long long)(V - m0) * d * 4;
     if (rem <= 0) return;
     const int nrec = rem > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)rem;
@@ -836,6 +839,47 @@ struct EpiDw {
     for (int cb = 0; cb < NCB; ++cb) {
       const int j = n0 + cb * 32 + (lane & 31);
       vo[cb] = j < d ? (((lane >> 5) * 4 * d + j) * 4) : (int)0x80000000;
+    }
+    if constexpr (NCB == 2 && NRB % 2 == 0) {
+      if (accumulate && lds_rmw) {
+        // Read-modify-write through the wave's own LDS slice (the tile belongs to one
+        // workgroup per launch, so plain loads and stores suffice): 64 rows of the wave's
+        // 64 columns per pass, copied by the buffer unit as 16 loads of 4 rows x 256 B,
+        // each placed 1088 B apart so that rows r and r + 4 (the two half-waves of a read)
+        // fall in different banks; then each lane adds and stores its own elements.
+        // Rows v >= V read zero and are not stored; columns j >= d are not stored.
+        constexpr int PITCH = 1088;
+        LDS_AS char *slice = (LDS_AS char *)smem + (threadIdx.x >> 6) * (16 * PITCH);
+#pragma unroll
+        for (int ps = 0; ps < NRB / 2; ++ps) {
+          if (ps > 0) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): last pass's reads
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (LDS_AS void *)(slice + k * PITCH), 16,
+                ((ps * 64 + 4 * k + (lane >> 4)) * d + n0 + (lane & 15) * 4) * 4, 0, 0,
+                16 /* cache policy sc1: through L2 only */);
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+#pragma unroll
+          for (int r2 = 0; r2 < 2; ++r2) {
+            const int rb = ps * 2 + r2;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int rp = r2 * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);  // row in pass
+              const int roff = (rb * 32 + (i >> 2) * 8 + (i & 3)) * d * 4;
+#pragma unroll
+              for (int cb = 0; cb < NCB; ++cb) {
+                const float old = *(const LDS_AS float *)(slice + (rp >> 2) * PITCH +
+                                                          (rp & 3) * 256 +
+                                                          (cb * 32 + (lane & 31)) * 4);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rb][cb][i] + old), rs,
+                                                      vo[cb] + roff, 0, 0);
+              }
+            }
+          }
+        }
+        return;
+      }
     }
     if (accumulate) {
 #pragma unroll
@@ -1456,7 +1500,7 @@ hipError_t launch_dw_gemm(int dtype, const void *dz, const void *dzt, const void
                           hipStream_t s) {
   // D[v][j] = sum_c dz[c][v] h[c][j] over k tokens
   GemmGrid G{cdiv(V, tile_rows(dtype)), cdiv(d, kTile), 1, (int)k, (int)k, 0};
-  EpiDw e{dW, (int)d, (int)V, accumulate};
+  EpiDw e{dW, (int)d, (int)V, accumulate, dtype == 1};
   if (dtype == 1) {
     // A = dzT ([v][c]), B = hT ([j][c]): both token-contiguous (KC), in blocks of 256
     // tokens ([V_pad][256] and [d][256] each)
