@@ -76,12 +76,14 @@ class ClockSampler:
     def result(self):
         if not self.mhz:
             return None
-        return {"gfx_mhz_mean": round(float(np.mean(self.mhz)), 1),
+        return {"gfx_mhz_median": round(float(np.median(self.mhz)), 1),
                 "gfx_mhz_min": round(float(np.min(self.mhz)), 1),
-                "socket_power_w_mean": round(float(np.mean(self.watts)), 1) if self.watts else None,
+                "gfx_mhz_max": round(float(np.max(self.mhz)), 1),
+                "socket_power_w_median": (round(float(np.median(self.watts)), 1)
+                                          if self.watts else None),
                 "samples": len(self.mhz),
                 "source": "amd-smi current graphics clock and socket power, sampled every 5 ms "
-                          "over the timed steps"}
+                          "over the timed steps (the reading changes slowly; indicative only)"}
 
 
 def warm_up(step, n, seconds=0.5):
@@ -763,7 +765,7 @@ def main():
         "clock_observed": clk.result(),
         "frac_of_peak_at_observed_clock": (
             None if clk.result() is None
-            else round(tflops / (peak * clk.result()["gfx_mhz_mean"] / 2400.0), 4)),
+            else round(tflops / (peak * clk.result()["gfx_mhz_median"] / 2400.0), 4)),
         "peak_mem_gib": round(peak_gib, 3),
         "loss": loss_val,
         "roofline": roofline,
