@@ -191,10 +191,16 @@ def parse():
 
 
 def kernel_source_hash(files=("kd_kernels.hip", "kd_api.hip", "kd_internal.h")):
+    """Hash of the sources that the counters were taken on, comments and whitespace
+    removed: a change of the code (not of its comments) makes the record stale."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "output_head_kl_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "output_head_kl_amd", "csrc", f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)     # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                   # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

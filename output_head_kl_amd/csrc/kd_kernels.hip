@@ -812,9 +812,10 @@ struct EpiDhPart {
 
 // dW: tile rows are vocabulary entries v, columns hidden units j, so each accumulator
 // register holds 32 consecutive floats of two dW rows (one per half-wave).  The first
-// chunk stores; later chunks add with one fire-and-forget atomic per element, so the
-// workgroup does not wait for dW to be read back and the result does not depend on
-// timing (each element gets exactly one addition per launch, launches are ordered).
+// chunk group stores; later groups add.  Each element gets exactly one addition per
+// launch and launches are ordered, so the result does not depend on timing: the bf16
+// kernel reads the old values through LDS and stores the sums, the fp32 kernel adds with
+// one fire-and-forget atomic per element.
 struct EpiDw {
   static constexpr bool kPrefetch = false;
   struct Pre {};
