@@ -8,6 +8,8 @@ logits).  Every full-size workload, the 262144-token one included, is also compa
 batch's own count) plus the whole dW of a 512-row sub-batch run through the same
 kernels, and its mean loss is checked against the per-row losses the GPU returns.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -57,6 +59,45 @@ def test_ragged_shapes_in_full(torch_cuda, dtype):
     inp.idx[3, 1] = inp.idx[3, 0]
     inp.idx[650, 6] = inp.idx[650, 2]
     _check_full(inp, run(inp, torch_cuda))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,K,d,N,chunk,repeat", [
+    (1, 1, 8, 5, 2, False),      # one vocabulary entry: q = 1, the loss is sum p log p
+    (1, 3, 8, 9, 4, True),       # one entry named three times in every row
+    (2, 1, 8, 33, 7, False),     # K = 1: the loss is M times the cross-entropy
+    (7, 1, 16, 300, 128, False),
+    (385, 2, 64, 257, 256, False),  # one vocabulary row past a 384-row tile
+])
+def test_degenerate_shapes(torch_cuda, dtype, V, K, d, N, chunk, repeat):
+    """Vocabularies of one and two entries, K = 1, the smallest d, a vocabulary one row
+    past a tile and chunks that split the batch unevenly, in full against the oracle."""
+    inp = synth.make(1, seed=1000 + V * 10 + K, N=N, d=d, V=V, K=1 if repeat else K,
+                     chunk=chunk, dtype=dtype)
+    if repeat:  # K entries of the only index, with probabilities that sum to M
+        inp.idx = np.zeros((N, K), np.int32)
+        inp.p = np.repeat(inp.p / K, K, axis=1).astype(np.float32)
+        inp.cfg = dataclasses.replace(inp.cfg, K=K)
+    inp.mask[N // 2] = 0
+    got = run(inp, torch_cuda)
+    if V > 1:
+        _check_full(inp, got)
+        return
+    # One entry: q = 1, dz = M * 1 - (the row's p) = 0 exactly, so the gradients are zero
+    # and a relative error has no scale; they must be at the rounding floor of dz (one
+    # bf16 rounding of s*M, then the subtraction), i.e. below 2^-7 of s*M*|W| (bf16) or
+    # 1e-6 of it (fp32); the loss, lse and gathered logits are compared as usual.
+    ref = oracle.forward_backward(inp.h64(), inp.W64(), inp.idx, inp.p, inp.mask)
+    tol = TOL[dtype]
+    assert rel(got["loss"][0], ref["loss"]) <= tol["loss"]
+    assert max_abs_rel(got["row_lse"], ref["row_lse"]) <= tol["loss"]
+    assert max_abs_rel(got["zg"], ref["zg"]) <= ZG_TOL
+    count = int((inp.mask != 0).sum())
+    dz_floor = (2.0 ** -7 if dtype == "bf16" else 1e-6) * K / count  # bound on |dz|
+    dh_max, dW_max = float(np.abs(got["dh"]).max()), float(np.abs(got["dW"]).max())
+    print(dtype, "V=1 dh", dh_max, "dW", dW_max, flush=True)
+    assert dh_max <= dz_floor * np.abs(inp.W64()).max()     # dh = dz * W[0]
+    assert dW_max <= dz_floor * np.abs(inp.h64()).max() * N  # dW[0] = sum_n dz[n] h[n]
 
 
 def test_token_tile_groups_with_a_partial_group(torch_cuda):
