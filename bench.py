@@ -289,6 +289,23 @@ def bench_topk(args):
                      "traffic": topk_traffic(workload)},
         "kernels": kt, "cpu_baseline": None,
     }
+    # For scale: a plain streaming read of the same logits by torch (a row sum), timed the
+    # same way, after the measured calls.
+    ref = lambda: x.sum(dim=1, dtype=torch.float32)
+    warm_up(ref, 20)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rs = []
+    for _ in range(10):
+        e0.record()
+        ref()
+        e1.record()
+        torch.cuda.synchronize()
+        rs.append(e0.elapsed_time(e1))
+    ref_ms = float(np.median(rs))
+    ref_gbs = N * V * 2 / (ref_ms * 1e-3) / 1e9
+    res["read_reference"] = {"op": "torch sum(logits, dim=1, dtype=float32), same tensor",
+                             "ms": round(ref_ms, 4), "GB/s": round(ref_gbs, 1),
+                             "producer_rate_over_it": round(ref_ms / kern_ms, 4)}
     if args.copy_gib > 0:
         n = int(args.copy_gib * 2**30) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
