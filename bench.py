@@ -501,6 +501,35 @@ def memory_sweep(dw_group_tokens=None):
     print(json.dumps(res), flush=True)
 
 
+def gemm_reference(torch, h, W, cfg, fwd_ms):
+    """For scale: torch's plain GEMM (hipBLASLt) on the forward GEMM's shape, one chunk of
+    tokens against the whole W, bf16 in and out, with no epilogue at all (no logsumexp, no
+    gather, no exponentials kept).  Both operand orders; median of 10 event-timed calls
+    each, after 0.5 s of calls."""
+    import torch.nn.functional as F
+    hc = h[:cfg.chunk]
+    forms = {"linear(W, h_c): [V, chunk] out": lambda: F.linear(W, hc),
+             "linear(h_c, W): [chunk, V] out": lambda: F.linear(hc, W)}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    got = {}
+    for name, fn in forms.items():
+        warm_up(fn, 3)
+        ts = []
+        for _ in range(10):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        got[name] = round(float(np.median(ts)), 4)
+    best = min(got.values())
+    flops = 2.0 * cfg.chunk * cfg.V * cfg.d
+    return {"op": "torch.nn.functional.linear (hipBLASLt), bf16, one chunk, no epilogue",
+            "ms": got, "best_tflops": round(flops / (best * 1e-3) / 1e12, 1),
+            "fwd_gemm_lse_ms": round(fwd_ms, 4),
+            "fwd_gemm_lse_speed_over_it": round(best / fwd_ms, 4)}
+
+
 def _kernel_table(ktimes, steps):
     out = {}
     for name, (tot, n) in ktimes.items():
@@ -819,6 +848,8 @@ def main():
             "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
             "loss": float(out0[0].item())}
         del out0, ws0
+    if cfg.dtype == "bf16" and roofline is not None and roofline["kernel"] == "fwd_gemm_lse":
+        res["gemm_reference"] = gemm_reference(torch, h, W, cfg, kernels["fwd_gemm_lse"]["avg_ms"])
     if args.copy_gib > 0:
         n = int(args.copy_gib * 2**30) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
