@@ -28,8 +28,10 @@ GEMM_CLASSES = ("fwd_gemm_lse", "bwd_gemm_dz", "dh_gemm", "dw_gemm")
 
 class ClockSampler:
     """While active, samples the GPU's current graphics clock and socket power through
-    amd-smi every `period` seconds in a thread; `result()` gives their means over the
-    samples, or None where amd-smi is not available (one GPU visible to it only)."""
+    amd-smi every `period` seconds in a thread; `result()` gives their medians and range
+    over the samples, or None where amd-smi is not available (one GPU visible to it only).
+    The reading lags and some boxes report an idle value under load, so the bench line's
+    clock_observed comes from in-kernel counters (unit_clocks) and this is kept beside it."""
 
     def __init__(self, period=0.005):
         self.period, self.mhz, self.watts, self._stop = period, [], [], None
@@ -84,6 +86,23 @@ class ClockSampler:
                 "samples": len(self.mhz),
                 "source": "amd-smi current graphics clock and socket power, sampled every 5 ms "
                           "over the timed steps (the reading changes slowly; indicative only)"}
+
+
+CLOCK_GROUPS = 2048   # one-wave workgroups per clock stamp: eight per compute unit
+
+
+def unit_clocks(before, after, khz):
+    """Average shader clock in MHz of each compute unit between two kd_clock_stamp records
+    (int64 arrays of 3 * n_groups words).  Stamps are paired unit by unit: the cycle
+    counters of different units are not aligned with each other."""
+    def per_unit(rec):
+        out = {}
+        for ident, cyc, tick in np.asarray(rec, dtype=np.int64).reshape(-1, 3).tolist():
+            out.setdefault(((ident >> 32) & 15, (ident >> 8) & 0xFF), (cyc, tick))
+        return out
+    a, b = per_unit(before), per_unit(after)
+    return np.array([(b[k][0] - c0) / (b[k][1] - t0) * khz / 1000.0
+                     for k, (c0, t0) in a.items() if k in b and b[k][1] > t0])
 
 
 def warm_up(step, n, seconds=0.5):
@@ -732,8 +751,18 @@ def main():
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
     prof = not args.no_profile
+    stamps = torch.zeros((2, 3 * CLOCK_GROUPS), dtype=torch.int64, device=dev)
+    kd.clock_stamp(stamps[0])
     with ClockSampler() as clk:
         step_ms, out = timed_steps(step, args.steps)
+    kd.clock_stamp(stamps[1])
+    mhz = unit_clocks(stamps[0].cpu().numpy(), stamps[1].cpu().numpy(), kd.wall_clock_khz())
+    clock = None if mhz.size == 0 else {
+        "gfx_mhz_median": round(float(np.median(mhz)), 1),
+        "gfx_mhz_min": round(float(mhz.min()), 1), "gfx_mhz_max": round(float(mhz.max()), 1),
+        "compute_units": int(mhz.size),
+        "source": "each compute unit's shader cycle counter against the constant-rate counter, "
+                  "stamped by kd_clock_stamp right before and after the timed steps"}
     loss_val = float(out[0].item())
     del out
     ms_profiled = None
@@ -814,10 +843,10 @@ def main():
         "frac_of_peak_executed": round(tflops / peak, 4),
         "tflops_recompute_equiv_8NVd": round(tflops_recompute_equiv, 1),
         # the peak assumes 2.4 GHz; against the clock the chip actually ran at
-        "clock_observed": clk.result(),
+        "clock_observed": clock,
         "frac_of_peak_at_observed_clock": (
-            None if clk.result() is None
-            else round(tflops / (peak * clk.result()["gfx_mhz_median"] / 2400.0), 4)),
+            None if clock is None else round(tflops / (peak * clock["gfx_mhz_median"] / 2400.0), 4)),
+        "clock_amdsmi": clk.result(),
         "peak_mem_gib": round(peak_gib, 3),
         "loss": loss_val,
         "roofline": roofline,

@@ -329,7 +329,7 @@ int kd_teacher_topk_noalloc(const void *logits, int32_t dtype, int64_t N, int64_
 /* Text describing the last non-OK return on the calling thread ("" if none). */
 const char *kd_last_error(void);
 
-/* Library interface version: 3 (it increments when a call is added or changes). */
+/* Library interface version: 4 (it increments when a call is added or changes). */
 int kd_version(void);
 
 /*
@@ -344,6 +344,22 @@ int kd_profile_enable(int on);
 int kd_profile_num_classes(void);
 const char *kd_profile_class_name(int cls);
 int kd_profile_read(int cls, double *total_ms, int64_t *launches);
+
+/*
+ * Clock measurement for benchmarks (not part of the loss).  kd_clock_stamp enqueues on
+ * `stream` one kernel of n_groups one-wave workgroups; workgroup g writes three words at
+ * stamps[3g]: the compute unit it ran on (accelerator complex in bits 35:32, the
+ * hardware-id register in bits 31:0, whose bits 15:8 number the unit within it), that
+ * unit's shader cycle counter, and the device's constant-rate counter.  With n_groups a
+ * few times the number of compute units every unit writes at least one stamp.  Two
+ * stamps around some work, paired unit by unit (the cycle counters of different units
+ * are not aligned), give each unit's average shader clock over the work: cycles /
+ * constant ticks * kd_wall_clock_khz().  stamps: device memory for 3 * n_groups uint64,
+ * 8-byte aligned, caller-owned; 1 <= n_groups <= 65536, else KD_E_ARG.
+ * kd_wall_clock_khz writes the constant counter's rate in kHz (current device).
+ */
+int kd_clock_stamp(uint64_t *stamps, int32_t n_groups, void *stream);
+int kd_wall_clock_khz(int32_t *khz_out);
 
 #ifdef __cplusplus
 }

@@ -89,6 +89,10 @@ def _lib():
     lib.kd_profile_class_name.restype = ctypes.c_char_p
     lib.kd_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.kd_clock_stamp.argtypes = [vp, i32, vp]
+    lib.kd_clock_stamp.restype = ctypes.c_int
+    lib.kd_wall_clock_khz.argtypes = [ctypes.POINTER(i32)]
+    lib.kd_wall_clock_khz.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -481,6 +485,25 @@ def profile_enable(on: bool = True) -> None:
 def profile_classes():
     lib = _lib()
     return [lib.kd_profile_class_name(i).decode() for i in range(lib.kd_profile_num_classes())]
+
+
+def clock_stamp(stamps, stream=None) -> None:
+    """Enqueues kd_clock_stamp into ``stamps``, a contiguous int64 CUDA tensor of
+    3 * n_groups elements (per workgroup: compute unit, its cycle counter, the constant
+    counter)."""
+    import torch
+    if stamps.dtype != torch.int64 or not stamps.is_contiguous() or stamps.numel() % 3:
+        raise ValueError("stamps must be a contiguous int64 tensor of 3 * n_groups elements")
+    _on_device(stamps.device, stamps=stamps)
+    _check(_lib().kd_clock_stamp(_ptr(stamps), stamps.numel() // 3,
+                                 _stream(stream, stamps.device)))
+
+
+def wall_clock_khz() -> int:
+    """Rate of the constant counter that kd_clock_stamp records, in kHz."""
+    out = ctypes.c_int32(0)
+    _check(_lib().kd_wall_clock_khz(ctypes.byref(out)))
+    return int(out.value)
 
 
 def profile_read():

@@ -188,7 +188,7 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
 
 extern "C" {
 
-int kd_version(void) { return 3; }
+int kd_version(void) { return 4; }
 
 const char *kd_last_error(void) { return g_err; }
 
@@ -629,6 +629,26 @@ int kd_teacher_topk_noalloc(const void *logits, int32_t dtype, int64_t N, int64_
   HIPCHK(kd::topk_scratch(&flags));
   return topk_run(logits, dtype, N, V, K, topk_idx, topk_p, row_lse, flags,
                   (hipStream_t)stream_v);
+}
+
+int kd_clock_stamp(uint64_t *stamps, int32_t n_groups, void *stream_v) {
+  g_err[0] = 0;
+  if (!stamps) return fail(KD_E_ARG, "stamps is null");
+  if ((uintptr_t)stamps % 8) return fail(KD_E_ARG, "stamps must be 8-byte aligned");
+  if (n_groups < 1 || n_groups > 65536)
+    return fail(KD_E_ARG, "n_groups = %d outside [1, 65536]", n_groups);
+  HIPCHK(kd::launch_clock_stamp((unsigned long long *)stamps, n_groups, (hipStream_t)stream_v));
+  return KD_OK;
+}
+
+int kd_wall_clock_khz(int32_t *khz_out) {
+  g_err[0] = 0;
+  if (!khz_out) return fail(KD_E_ARG, "khz_out is null");
+  int dev = 0, khz = 0;
+  HIPCHK(hipGetDevice(&dev));
+  HIPCHK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+  *khz_out = khz;
+  return KD_OK;
 }
 
 int kd_profile_enable(int on) {

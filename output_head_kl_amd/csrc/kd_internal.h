@@ -64,6 +64,7 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
 
 // --- launchers (all asynchronous on `s`; return hipSuccess or the launch error) ---
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_clock_stamp(unsigned long long *out, int groups, hipStream_t s);
 hipError_t launch_validate(const int32_t *idx, const float *p, int64_t NK, int64_t V,
                            const uint8_t *mask, int64_t N, int *flags,
                            unsigned long long *count, hipStream_t s);

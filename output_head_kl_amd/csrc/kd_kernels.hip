@@ -1570,6 +1570,28 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Clock measurement (benchmarks only): lane 0 of each one-wave workgroup writes the
+// identity of its compute unit (XCC_ID in bits 35:32, HW_ID in bits 31:0: its SE, SH and
+// CU numbers are bits 15:8), the unit's shader cycle counter and the device's
+// constant-rate counter.  The cycle counters of different units are not aligned, so two
+// stamps are compared unit by unit.
+constexpr int kHwRegXccId = 20 | ((4 - 1) << 11);   // hwreg(XCC_ID, 0, 4)
+constexpr int kHwRegHwId = 4 | ((32 - 1) << 11);    // hwreg(HW_ID, 0, 32)
+__global__ __launch_bounds__(64) void k_clock_stamp(unsigned long long *out) {
+  if (threadIdx.x != 0) return;
+  const unsigned xcc = __builtin_amdgcn_s_getreg(kHwRegXccId) & 15u;
+  const unsigned hw = __builtin_amdgcn_s_getreg(kHwRegHwId);
+  unsigned long long *o = out + 3 * (long long)blockIdx.x;
+  o[0] = ((unsigned long long)xcc << 32) | hw;
+  o[1] = clock64();
+  o[2] = wall_clock64();
+}
+
+hipError_t launch_clock_stamp(unsigned long long *out, int groups, hipStream_t s) {
+  hipLaunchKernelGGL(k_clock_stamp, dim3((unsigned)groups), dim3(64), 0, s, out);
+  return hipGetLastError();
+}
+
 // flags[0] |= 1 for an index outside [0, V) or a probability that is negative or not
 // finite; count += number of nonzero mask bytes.
 __global__ void k_validate(const int32_t *idx, const float *p, long long NK, int V,

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_profile_classes(lib):
-    assert lib.kd_version() == 3
+    assert lib.kd_version() == 4
     names = kd.profile_classes()
     assert "fwd_gemm_lse" in names and "dw_gemm" in names and len(names) == len(set(names))
 
@@ -332,3 +332,14 @@ def test_scale_grads_rejects_bad_calls_on_host(lib, kw, code):
 
 def test_scale_grads_with_nothing_to_scale_does_nothing(lib):
     assert _call_scale(lib, N=0, V=0, dh32=None, dh=None, dW=None) == OK
+
+
+def test_clock_stamp_rejects_bad_arguments_before_any_gpu_work(lib):
+    """kd_clock_stamp and kd_wall_clock_khz check their arguments on the host first, so
+    these calls return KD_E_ARG without touching a device (none is needed here)."""
+    assert lib.kd_clock_stamp(None, 8, None) == E_ARG
+    assert lib.kd_last_error()
+    assert lib.kd_clock_stamp(0x1004, 8, None) == E_ARG          # not 8-byte aligned
+    assert lib.kd_clock_stamp(0x1000, 0, None) == E_ARG
+    assert lib.kd_clock_stamp(0x1000, 65537, None) == E_ARG
+    assert lib.kd_wall_clock_khz(None) == E_ARG
