@@ -172,6 +172,10 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="token rows of the workload timed through the CPU oracle (a bounded "
                          "sample: ~15-25 s of host time at the full vocabulary)")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the torch kernels timed for scale (gemm_reference of the fused "
+                         "call, read_reference of --topk), e.g. so that a kernel trace holds the "
+                         "library's kernels only")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip per-kernel HIP-event timing inside the timed region")
     ap.add_argument("--split", action="store_true",
@@ -267,6 +271,26 @@ def topk_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def read_reference(torch, x, N, V, kern_ms):
+    """torch's row sum over the teacher logits (a plain streaming read of the same bytes):
+    median of 10 HIP-event-timed calls after 0.5 s of calls."""
+    ref = lambda: x.sum(dim=1, dtype=torch.float32)
+    warm_up(ref, 20)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rs = []
+    for _ in range(10):
+        e0.record()
+        ref()
+        e1.record()
+        torch.cuda.synchronize()
+        rs.append(e0.elapsed_time(e1))
+    ref_ms = float(np.median(rs))
+    ref_gbs = N * V * 2 / (ref_ms * 1e-3) / 1e9
+    return {"op": "torch sum(logits, dim=1, dtype=float32), same tensor",
+            "ms": round(ref_ms, 4), "GB/s": round(ref_gbs, 1),
+            "producer_rate_over_it": round(ref_ms / kern_ms, 4)}
+
+
 def bench_topk(args):
     """Teacher top-K cache producer: one row of logits per token, read once (HBM-bound)."""
     import torch
@@ -310,21 +334,8 @@ def bench_topk(args):
     }
     # For scale: a plain streaming read of the same logits by torch (a row sum), timed the
     # same way, after the measured calls.
-    ref = lambda: x.sum(dim=1, dtype=torch.float32)
-    warm_up(ref, 20)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    rs = []
-    for _ in range(10):
-        e0.record()
-        ref()
-        e1.record()
-        torch.cuda.synchronize()
-        rs.append(e0.elapsed_time(e1))
-    ref_ms = float(np.median(rs))
-    ref_gbs = N * V * 2 / (ref_ms * 1e-3) / 1e9
-    res["read_reference"] = {"op": "torch sum(logits, dim=1, dtype=float32), same tensor",
-                             "ms": round(ref_ms, 4), "GB/s": round(ref_gbs, 1),
-                             "producer_rate_over_it": round(ref_ms / kern_ms, 4)}
+    if not args.no_reference:
+        res["read_reference"] = read_reference(torch, x, N, V, kern_ms)
     if args.copy_gib > 0:
         n = int(args.copy_gib * 2**30) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -877,7 +888,8 @@ def main():
             "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
             "loss": float(out0[0].item())}
         del out0, ws0
-    if cfg.dtype == "bf16" and roofline is not None and roofline["kernel"] == "fwd_gemm_lse":
+    if (cfg.dtype == "bf16" and roofline is not None and roofline["kernel"] == "fwd_gemm_lse"
+            and not args.no_reference):
         res["gemm_reference"] = gemm_reference(torch, h, W, cfg, kernels["fwd_gemm_lse"]["avg_ms"])
     if args.copy_gib > 0:
         n = int(args.copy_gib * 2**30) // 4
