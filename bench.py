@@ -705,6 +705,10 @@ def bench_shard(args, kd, torch, cfg, h, W, idx, p, mask):
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
+              "multi-GPU path (no collectives or sharding across GPUs).", file=sys.stderr)
+        sys.exit(2)
     if args.memory_sweep:
         memory_sweep(args.dw_group_tokens)
         return
@@ -712,15 +716,8 @@ def main():
         torch_baselines()
         return
     if args.topk:
-        if args.gpus != 1:
-            print("bench.py runs on one GPU only", file=sys.stderr)
-            sys.exit(2)
         bench_topk(args)
         return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
-              "multi-GPU path (no collectives or sharding across GPUs).", file=sys.stderr)
-        sys.exit(2)
     import torch
 
     import output_head_kl_amd as kd
