@@ -308,8 +308,9 @@ int kd_teacher_topk(const void *logits, int32_t dtype, int64_t N, int64_t V, int
 
 /*
  * kd_teacher_topk_noalloc -- kd_teacher_topk for callers that cannot allocate device
- * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc): no workspace argument and no allocation of any kind.
+ * memory (tight serving loops, harnesses that forbid hipMalloc): no workspace argument
+ * and no allocation of any kind.  Like kd_teacher_topk it synchronises its stream once
+ * to report bad rows, so it cannot be recorded into a HIP graph.
  *
  * The 256-byte workspace of kd_teacher_topk (one validity flag) is replaced by a
  * static module array of 256 bytes that every device the library runs on holds from
