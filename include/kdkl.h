@@ -144,6 +144,34 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kd_chunked_kl_fwd_bwd_async -- kd_chunked_kl_fwd_bwd with no host synchronisation, so
+ * that a caller can record it into a HIP graph and replay it (or keep the host ahead of
+ * the device).
+ *
+ * Arguments as kd_chunked_kl_fwd_bwd, plus
+ *   status  [1]  int32  device memory, written on the stream after the outputs: KD_OK, or
+ *                       KD_E_INDEX when a teacher entry is invalid (an index outside
+ *                       [0, V), a probability negative or not finite).
+ * With valid entries the outputs equal kd_chunked_kl_fwd_bwd's bit for bit.  With an
+ * invalid entry the whole sequence still runs and the outputs are undefined, but no
+ * kernel addresses memory outside the arguments and the workspace through it (indices
+ * outside the padded vocabulary are skipped).  A mask with no counted token gives loss
+ * 0, dh 0 and dW 0 through the same sequence.  The return value covers the host-side
+ * checks (KD_E_ARG, KD_E_UNSUPPORTED, KD_E_WORKSPACE, with nothing enqueued) and
+ * KD_E_HIP for a failed launch.  Every device operation is a kernel launch on `stream`
+ * (no memset or copy), and the sequence depends only on the sizes, the pointers and the
+ * workspace size, so a recorded graph replays it for new contents of the same buffers.
+ * The kernel timing of kd_profile_enable must be off while recording.
+ */
+int kd_chunked_kl_fwd_bwd_async(const void *h, const void *W, int32_t dtype,
+                                const int32_t *topk_idx, const float *topk_p,
+                                const uint8_t *loss_mask,
+                                int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                                float *loss, void *dh, float *dW,
+                                float *row_loss, float *row_lse, float *zg, int32_t *status,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kd_chunked_kl_fwd_bwd_f32dh -- kd_chunked_kl_fwd_bwd with dh written in float32.
  *
  * The pages' loss is an autograd function of the hidden states (codewithpapers.app
@@ -245,7 +273,8 @@ int kd_chunked_kl_bwd(const void *h, const void *W, int32_t dtype,
  *   row_lse[n] = M + log sum_g shard_sumexp[g,n] exp(shard_max[g,n] - M), M = max_g,
  *   l[n] = sum_k p log p - sum_g shard_pz[g,n] + (sum_k p) row_lse[n],
  *   loss = sum_n mask[n] l[n] / count; row_loss[n] = mask[n] ? l[n] : 0 (optional).
- *   Workspace: kd_vocab_shard_combine_workspace_bytes(N).  One stream synchronisation.
+ *   Workspace: kd_vocab_shard_combine_workspace_bytes(N).  No host synchronisation: the
+ *   count divides the loss on the device.
  * kd_vocab_shard_bwd: with the global row_lse and the upstream gradient g
  *   (grad_loss[0], on the device), for v in the shard
  *   dz[n,v] = g (mask[n]/count) (M[n] exp(z[n,v] - row_lse[n]) - sum_{k: idx=v} p[n,k]),
@@ -330,7 +359,7 @@ int kd_teacher_topk_noalloc(const void *logits, int32_t dtype, int64_t N, int64_
 /* Text describing the last non-OK return on the calling thread ("" if none). */
 const char *kd_last_error(void);
 
-/* Library interface version: 4 (it increments when a call is added or changes). */
+/* Library interface version: 5 (it increments when a call is added or changes). */
 int kd_version(void);
 
 /*

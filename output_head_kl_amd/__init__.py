@@ -52,6 +52,9 @@ def _lib():
     lib.kd_chunked_kl_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
                                           vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_fwd_bwd.restype = ctypes.c_int
+    lib.kd_chunked_kl_fwd_bwd_async.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i64,
+                                                vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_chunked_kl_fwd_bwd_async.restype = ctypes.c_int
     lib.kd_chunked_kl_fwd_bwd_f32dh.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32,
                                                 i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_fwd_bwd_f32dh.restype = ctypes.c_int
@@ -224,6 +227,36 @@ def fwd_bwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: boo
     if rows:
         return loss, dh, dW, row_loss, row_lse, zg
     return loss, dh, dW
+
+
+def fwd_bwd_async(h, W, topk_idx, topk_p, loss_mask, loss, dh, dW, status, workspace,
+                  chunk: int = 2048, row_loss=None, row_lse=None, zg=None, stream=None) -> None:
+    """kd_chunked_kl_fwd_bwd_async: the one-call loss into caller-given outputs with no host
+    synchronisation, so that it can be recorded into a graph (torch.cuda.graph) and
+    replayed.  Outputs as ``fwd_bwd`` returns them (loss [1] f32, dh [N, d] h's dtype,
+    dW [V, d] f32, optional row outputs); ``status`` is a [1] int32 CUDA tensor set to 0,
+    or to 2 (KD_E_INDEX) when a teacher entry is invalid (then the outputs are undefined).
+    ``workspace`` is required (a recorded graph must not allocate)."""
+    import torch
+    if workspace is None:
+        raise ValueError("workspace is required (a recorded graph must not allocate)")
+    dt, N, d, V, K, loss_mask = _prep(h, W, topk_idx, topk_p, loss_mask)
+    dev = h.device
+    _on_device(dev, loss=loss, dh=dh, dW=dW, status=status, row_loss=row_loss,
+               row_lse=row_lse, zg=zg)
+    _check_workspace(workspace, dev)
+    want = [(loss, (1,), torch.float32), (dh, (N, d), h.dtype), (dW, (V, d), torch.float32),
+            (status, (1,), torch.int32), (row_loss, (N,), torch.float32),
+            (row_lse, (N,), torch.float32), (zg, (N, K), torch.float32)]
+    for t, shape, dtype in want:
+        if t is not None and (tuple(t.shape) != shape or t.dtype != dtype
+                              or not t.is_contiguous()):
+            raise ValueError(f"an output has shape {tuple(t.shape)} and dtype {t.dtype}; "
+                             f"expected contiguous {shape} {dtype}")
+    _check(_lib().kd_chunked_kl_fwd_bwd_async(
+        _ptr(h), _ptr(W), dt, _ptr(topk_idx), _ptr(topk_p), _ptr(loss_mask), N, d, V, K, chunk,
+        _ptr(loss), _ptr(dh), _ptr(dW), _ptr(row_loss), _ptr(row_lse), _ptr(zg), _ptr(status),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
 
 
 def fwd(h, W, topk_idx, topk_p, loss_mask=None, chunk: int = 2048, rows: bool = False,

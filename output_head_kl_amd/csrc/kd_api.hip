@@ -188,7 +188,7 @@ bool make_layout(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int 
 
 extern "C" {
 
-int kd_version(void) { return 4; }
+int kd_version(void) { return 5; }
 
 const char *kd_last_error(void) { return g_err; }
 
@@ -233,8 +233,11 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
         int64_t chunk, float *loss, void *dh, float *dW, float *row_loss, float *row_lse,
         float *zg, const float *lse_in, const float *grad_loss, void *workspace,
         size_t workspace_bytes, void *stream_v, const ShardArgs &sh = ShardArgs(),
-        bool dh_f32 = false) {
+        bool dh_f32 = false, int32_t *status = nullptr) {
   g_err[0] = 0;
+  // status given: the one-call form without its host synchronisation (validity reported
+  // on the device through *status, the count used on the device only)
+  const bool async = status != nullptr;
   int rc = check_sizes(N, d, V, K, chunk, dtype);
   if (rc != KD_OK) return rc;
   const bool shard = mode == M_SFWD || mode == M_SBWD;
@@ -280,6 +283,8 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
   char *ws = (char *)workspace;
   int *flags = (int *)(ws + L.off_flags);
   unsigned long long *dcount = (unsigned long long *)(ws + L.off_flags + 8);
+  unsigned long long *dcount_eff = (unsigned long long *)(ws + L.off_flags + 16);
+  float *dinv = (float *)(ws + L.off_flags + 24);
   double *acc = (double *)(ws + L.off_acc);
   float2 *partials = (float2 *)(ws + L.off_partials);
   float *lse = (float *)(ws + L.off_lse);
@@ -303,24 +308,35 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
   if (N == 0) {
     if (fwd && !shard) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(loss, 4, stream));
     if (bwd) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(dW, (size_t)V * d * 4, stream));
+    if (async) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(status, 4, stream));
     return KD_OK;
   }
 
-  // Validate the teacher entries and count the mask; the only host synchronisation.
+  // Validate the teacher entries and count the mask; the count and its reciprocal stay on
+  // the device for the kernels that scale by them.  The synchronising form reads the
+  // result back here (its only host synchronisation); the asynchronous one does not, and
+  // runs the whole sequence whatever it finds (kernels skip indices outside the padded
+  // vocabulary, and a count of zero scales every gradient to zero).
   LAUNCH(kd::KC_MISC, kd::launch_fill_zero(ws + L.off_flags, L.off_acc - L.off_flags + 64, stream));
   LAUNCH(kd::KC_VALIDATE,
          kd::launch_validate(topk_idx, topk_p, N * (int64_t)K, V_idx, loss_mask, N, flags, dcount,
                              stream));
-  struct {
-    int flags[2];
-    unsigned long long count;
-  } hostv;
-  HIPCHK(hipMemcpyAsync(&hostv, flags, sizeof hostv, hipMemcpyDeviceToHost, stream));
-  HIPCHK(hipStreamSynchronize(stream));
-  if (hostv.flags[0])
-    return fail(KD_E_INDEX, "a teacher index is outside [0, %lld) or a probability is negative or not finite",
-                (long long)V_idx);
-  const int64_t count = loss_mask ? (int64_t)hostv.count : N;
+  LAUNCH(kd::KC_MISC, kd::launch_count_prep(dcount, loss_mask != nullptr, N, dcount_eff, dinv,
+                                            stream));
+  int64_t count = -1;  // unknown on the host in the asynchronous form
+  if (!async) {
+    struct {
+      int flags[2];
+      unsigned long long count;
+    } hostv;
+    HIPCHK(hipMemcpyAsync(&hostv, flags, sizeof hostv, hipMemcpyDeviceToHost, stream));
+    HIPCHK(hipStreamSynchronize(stream));
+    if (hostv.flags[0])
+      return fail(KD_E_INDEX,
+                  "a teacher index is outside [0, %lld) or a probability is negative or not finite",
+                  (long long)V_idx);
+    count = loss_mask ? (int64_t)hostv.count : N;
+  }
   const bool want_rows = row_loss || row_lse || zg;
 
   if (count == 0) {
@@ -331,8 +347,7 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
     }
     if (!fwd || !(want_rows || mode == M_SFWD)) return KD_OK;
   }
-  const bool backward = bwd && count > 0;
-  const float inv_count = count > 0 ? (float)(1.0 / (double)count) : 0.f;
+  const bool backward = bwd && count != 0;
   if (fwd) LAUNCH(kd::KC_MISC, kd::launch_fill_zero(bcount, (size_t)L.nkeys * 4, stream));
   void *WT = ws + L.off_wt;
   if (backward && dtype == KD_BF16)
@@ -359,7 +374,7 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
              kd::launch_buckets(idx_k, rows, K, L.tv, (int)(L.V_pad / L.tv), bcount, bcursor,
                                 boff, bent, stream));
       // the fused call keeps this chunk's exp(z - max) for its backward (no recompute)
-      void *u = (mode == M_FUSED && count > 0) ? dz : nullptr;
+      void *u = (mode == M_FUSED && count != 0) ? dz : nullptr;
       LAUNCH(kd::KC_FWD_GEMM, kd::launch_fwd_gemm(dtype, W, h_c, rows, d, V, partials, L.C_alloc,
                                                   boff, bent, zg_c, K, u, L.V_pad, L.C_alloc,
                                                   stream));
@@ -370,14 +385,14 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
         continue;
       }
       LAUNCH(kd::KC_COMBINE,
-             kd::launch_combine(partials, L.n_lse, L.C_alloc, zg_c, p_c, mask_c, rows, K, inv_count,
+             kd::launch_combine(partials, L.n_lse, L.C_alloc, zg_c, p_c, mask_c, rows, K, dinv,
                                 lse, sM, srow, rowterm, row_loss ? row_loss + c0 : nullptr,
                                 row_lse ? row_lse + c0 : nullptr, stream));
       if (count == 0) continue;  // forward-only sweep for the per-row outputs
       LAUNCH(kd::KC_MISC, kd::launch_accum_loss(rowterm, rows, acc, stream));
     } else {
       lse_c = lse_in + c0;
-      LAUNCH(kd::KC_COMBINE, kd::launch_row_scale(p_c, mask_c, rows, K, inv_count, grad_loss, sM,
+      LAUNCH(kd::KC_COMBINE, kd::launch_row_scale(p_c, mask_c, rows, K, dinv, grad_loss, sM,
                                                   srow, stream));
     }
     if (!backward) continue;
@@ -395,7 +410,7 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
       LAUNCH(kd::KC_BWD_GEMM, kd::launch_bwd_gemm(dtype, W, h_c, rows, d, V, lse_c, sM, dz, dzt_c,
                                                   tst_dz, L.V_pad, L.C_alloc, stream));
     LAUNCH(kd::KC_SCATTER, kd::launch_scatter(dtype, dz, dzt_c, tst_dz, L.C_alloc, idx_k, p_c, srow,
-                                              rows, K, stream));
+                                              rows, K, L.V_pad, stream));
     LAUNCH(kd::KC_DH_GEMM, kd::launch_dh_gemm(dtype, dz, W, WT, rows, d, V, L.V_pad, L.nsplit,
                                               L.k_split, dhpart, L.d_pad, L.C_alloc, stream));
     LAUNCH(kd::KC_DH_REDUCE,
@@ -412,8 +427,9 @@ int run(Mode mode, const void *h, const void *W, int32_t dtype, const int32_t *t
       ++dw_launches;
     }
   }
-  if (fwd && !shard && count > 0)
-    LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, count, loss, stream));
+  if (fwd && !shard && count != 0)
+    LAUNCH(kd::KC_MISC, kd::launch_finalize(acc, dcount_eff, loss, stream));
+  if (async) LAUNCH(kd::KC_MISC, kd::launch_status_out(flags, KD_E_INDEX, status, stream));
   return KD_OK;
 }
 
@@ -428,6 +444,20 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype, const int
                           size_t workspace_bytes, void *stream) {
   return run(M_FUSED, h, W, dtype, topk_idx, topk_p, loss_mask, N, d, V, K, chunk, loss, dh, dW,
              row_loss, row_lse, zg, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kd_chunked_kl_fwd_bwd_async(const void *h, const void *W, int32_t dtype,
+                                const int32_t *topk_idx, const float *topk_p,
+                                const uint8_t *loss_mask, int64_t N, int64_t d, int64_t V,
+                                int32_t K, int64_t chunk, float *loss, void *dh, float *dW,
+                                float *row_loss, float *row_lse, float *zg, int32_t *status,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  if (!status) return fail(KD_E_ARG, "status is required");
+  if ((uintptr_t)status % 4) return fail(KD_E_ARG, "status must be 4-byte aligned");
+  return run(M_FUSED, h, W, dtype, topk_idx, topk_p, loss_mask, N, d, V, K, chunk, loss, dh, dW,
+             row_loss, row_lse, zg, nullptr, nullptr, workspace, workspace_bytes, stream,
+             ShardArgs(), false, status);
 }
 
 int kd_chunked_kl_fwd_bwd_f32dh(const void *h, const void *W, int32_t dtype,
@@ -547,10 +577,11 @@ int kd_vocab_shard_combine(const float *shard_max, const float *shard_sumexp,
   }
   LAUNCH(kd::KC_VALIDATE, kd::launch_validate(nullptr, nullptr, 0, 1, loss_mask, N, flags, dcount,
                                               stream));
-  unsigned long long hc = 0;
-  HIPCHK(hipMemcpyAsync(&hc, dcount, sizeof hc, hipMemcpyDeviceToHost, stream));
-  HIPCHK(hipStreamSynchronize(stream));
-  const int64_t count = loss_mask ? (int64_t)hc : N;
+  // the count divides the loss on the device: no host synchronisation
+  unsigned long long *count = (unsigned long long *)(ws + 16);
+  float *inv_count = (float *)(ws + 24);
+  LAUNCH(kd::KC_MISC, kd::launch_count_prep(dcount, loss_mask != nullptr, N, count, inv_count,
+                                            stream));
   LAUNCH(kd::KC_COMBINE, kd::launch_shard_combine(shard_max, shard_sumexp, shard_pz, G, N, topk_p,
                                                   loss_mask, K, row_lse, row_loss, rowterm, stream));
   LAUNCH(kd::KC_MISC, kd::launch_accum_loss(rowterm, N, acc, stream));

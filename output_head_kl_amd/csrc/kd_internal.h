@@ -93,15 +93,21 @@ hipError_t launch_rescale_dz(int dtype, void *dz, void *dzt, int64_t tst, const 
                              int64_t V_pad, int64_t C_alloc, hipStream_t s);
 hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part,
                           const float *zg, const float *p_c, const uint8_t *mask_c,
-                          int64_t rows, int32_t K, float inv_count, float *lse, float *sM,
+                          int64_t rows, int32_t K, const float *inv_count, float *lse, float *sM,
                           float *srow, double *rowterm, float *row_loss, float *row_lse,
                           hipStream_t s);
 // Backward-only path: sM = g*mask*M/count, s = g*mask/count per token (g on the device).
 hipError_t launch_row_scale(const float *p_c, const uint8_t *mask_c, int64_t rows, int32_t K,
-                            float inv_count, const float *g, float *sM, float *srow,
+                            const float *inv_count, const float *g, float *sM, float *srow,
                             hipStream_t s);
 hipError_t launch_accum_loss(const double *rowterm, int64_t rows, double *acc, hipStream_t s);
-hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s);
+hipError_t launch_finalize(const double *acc, const unsigned long long *count, float *loss,
+                           hipStream_t s);
+// count[0] = the mask's count (or N without a mask), inv_count[0] = 1 / count (0 for none)
+hipError_t launch_count_prep(const unsigned long long *mask_count, bool has_mask, int64_t N,
+                             unsigned long long *count, float *inv_count, hipStream_t s);
+// status[0] = bad_code when flags[0] is raised, else 0
+hipError_t launch_status_out(const int *flags, int32_t bad_code, int32_t *status, hipStream_t s);
 // dh_out = g[0] * dh32 rounded once to dtype (bf16 RNE or fp32), dW *= g[0] in place (dW
 // untouched when g[0] == 1); dh32 and dW 16-byte aligned.
 hipError_t launch_scale_grads(int dtype, const float *g, const float *dh32, void *dh_out,
@@ -115,7 +121,7 @@ hipError_t launch_bwd_gemm(int dtype, const void *W, const void *h_c, int64_t ro
                            int64_t tst, int64_t V_pad, int64_t C_alloc, hipStream_t s);
 hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t tst, int64_t C_alloc,
                           const int32_t *idx_c, const float *p_c, const float *srow, int64_t rows,
-                          int32_t K, hipStream_t s);
+                          int32_t K, int64_t V_pad, hipStream_t s);
 // h chunk [rows][d] bf16 -> hT in the token-blocked layout (tst = d * 256), columns
 // c < C_alloc (zero for c >= rows).
 hipError_t launch_transpose_h(const void *h_c, int64_t rows, int64_t d, int64_t C_alloc,

@@ -1653,13 +1653,13 @@ __global__ void k_bucket_count(const int32_t *idx, int rows, int K, int tv, int 
     for (int i = t; i < ntm; i += blockDim.x) hist[i] = 0;
     __syncthreads();
     for (int e = t; e < n; e += blockDim.x)
-      if (ip[e] >= 0) atomicAdd(&hist[ip[e] / tv], 1);
+      if ((unsigned)ip[e] < (unsigned)(ntm * tv)) atomicAdd(&hist[ip[e] / tv], 1);
     __syncthreads();
     for (int i = t; i < ntm; i += blockDim.x)
       if (hist[i]) atomicAdd(&counts[i * ntn + tn], hist[i]);
   } else {
     for (int e = t; e < n; e += blockDim.x)
-      if (ip[e] >= 0) atomicAdd(&counts[(ip[e] / tv) * ntn + tn], 1);
+      if ((unsigned)ip[e] < (unsigned)(ntm * tv)) atomicAdd(&counts[(ip[e] / tv) * ntn + tn], 1);
   }
 }
 
@@ -1704,7 +1704,7 @@ __global__ void k_bucket_fill(const int32_t *idx, int rows, int K, int tv, int n
     for (int i = t; i < ntm; i += blockDim.x) hist[i] = 0;
     __syncthreads();
     for (int e = t; e < n; e += blockDim.x)
-      if (ip[e] >= 0) atomicAdd(&hist[ip[e] / tv], 1);
+      if ((unsigned)ip[e] < (unsigned)(ntm * tv)) atomicAdd(&hist[ip[e] / tv], 1);
     __syncthreads();
     for (int i = t; i < ntm; i += blockDim.x)
       if (hist[i]) {
@@ -1715,7 +1715,9 @@ __global__ void k_bucket_fill(const int32_t *idx, int rows, int K, int tv, int n
   }
   for (int e = t; e < n; e += blockDim.x) {
     const int v = ip[e];
-    if (v < 0) continue;  // outside this vocabulary shard
+    // negative: outside this vocabulary shard; past the padded vocabulary: an invalid entry
+    // that the validation scan reports (never bucketed, so never addressed)
+    if ((unsigned)v >= (unsigned)(ntm * tv)) continue;
     const int bin = v / tv, q = e / K, r = r0 + q, k = e - q * K;
     const int pos = lds ? base[bin] + atomicAdd(&hist[bin], 1)
                         : offsets[bin * ntn + tn] + atomicAdd(&cursor[bin * ntn + tn], 1);
@@ -1747,7 +1749,7 @@ hipError_t launch_buckets(const int32_t *idx_c, int64_t rows, int32_t K, int tv,
 constexpr int kCombWaves = 16;
 __global__ __launch_bounds__(64 * kCombWaves) void k_combine(
     const float2 *part, int n_lse, long long ld, const float *zg, const float *p,
-    const uint8_t *mask, int rows, int K, float inv_count, float *lse_out, float *sM_out,
+    const uint8_t *mask, int rows, int K, const float *inv_count_p, float *lse_out, float *sM_out,
     float *s_out, double *rowterm, float *row_loss, float *row_lse) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = blockIdx.x * 64 + lane;
@@ -1806,6 +1808,7 @@ __global__ __launch_bounds__(64 * kCombWaves) void k_combine(
     const double ell = h - pz + ms * (double)lse;
     const bool on = mask ? mask[r] != 0 : true;
     lse_out[r] = lse;
+    const float inv_count = inv_count_p[0];
     sM_out[r] = on ? (float)(ms * (double)inv_count) : 0.f;
     s_out[r] = on ? inv_count : 0.f;
     rowterm[r] = on ? ell : 0.0;
@@ -1816,7 +1819,7 @@ __global__ __launch_bounds__(64 * kCombWaves) void k_combine(
 
 hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part,
                           const float *zg, const float *p_c, const uint8_t *mask_c,
-                          int64_t rows, int32_t K, float inv_count, float *lse, float *sM,
+                          int64_t rows, int32_t K, const float *inv_count, float *lse, float *sM,
                           float *srow, double *rowterm, float *row_loss, float *row_lse,
                           hipStream_t s) {
   hipLaunchKernelGGL(k_combine, dim3(cdiv(rows, 64)), dim3(64 * kCombWaves), 0, s, partials,
@@ -1832,7 +1835,7 @@ hipError_t launch_combine(const float2 *partials, int64_t n_lse, int64_t ld_part
 // backward matches the fused call bit for bit.  g is read from device memory.
 __global__ __launch_bounds__(64 * kCombWaves) void k_row_scale(const float *p,
                                                                const uint8_t *mask, int rows,
-                                                               int K, float inv_count,
+                                                               int K, const float *inv_count_p,
                                                                const float *g, float *sM_out,
                                                                float *s_out) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1848,14 +1851,14 @@ __global__ __launch_bounds__(64 * kCombWaves) void k_row_scale(const float *p,
     double ms = 0.0;
     for (int i = 0; i < kCombWaves; ++i) ms += sd[i][lane];
     const bool on = mask ? mask[r] != 0 : true;
-    const float gg = g[0];
+    const float gg = g[0], inv_count = inv_count_p[0];
     sM_out[r] = on ? (float)(ms * (double)inv_count) * gg : 0.f;
     s_out[r] = on ? inv_count * gg : 0.f;
   }
 }
 
 hipError_t launch_row_scale(const float *p_c, const uint8_t *mask_c, int64_t rows, int32_t K,
-                            float inv_count, const float *g, float *sM, float *srow,
+                            const float *inv_count, const float *g, float *sM, float *srow,
                             hipStream_t s) {
   hipLaunchKernelGGL(k_row_scale, dim3(cdiv(rows, 64)), dim3(64 * kCombWaves), 0, s, p_c, mask_c,
                      (int)rows, (int)K, inv_count, g, sM, srow);
@@ -1881,12 +1884,45 @@ hipError_t launch_accum_loss(const double *rowterm, int64_t rows, double *acc, h
   return hipGetLastError();
 }
 
-__global__ void k_finalize(const double *acc, long long count, float *loss) {
-  if (threadIdx.x == 0) loss[0] = count > 0 ? (float)(acc[0] / (double)count) : 0.f;
+__global__ void k_finalize(const double *acc, const unsigned long long *count_p, float *loss) {
+  if (threadIdx.x == 0) {
+    const unsigned long long count = count_p[0];
+    loss[0] = count > 0 ? (float)(acc[0] / (double)count) : 0.f;
+  }
 }
 
-hipError_t launch_finalize(const double *acc, int64_t count, float *loss, hipStream_t s) {
-  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, s, acc, (long long)count, loss);
+hipError_t launch_finalize(const double *acc, const unsigned long long *count, float *loss,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, s, acc, count, loss);
+  return hipGetLastError();
+}
+
+// The number of counted tokens (the mask's nonzero bytes, or every token without a mask)
+// and its reciprocal, on the device, for the kernels that scale by them: with them there,
+// the sequence after the validation scan needs nothing back on the host.
+__global__ void k_count_prep(const unsigned long long *mask_count, int has_mask, long long N,
+                             unsigned long long *count, float *inv_count) {
+  if (threadIdx.x == 0) {
+    const unsigned long long c = has_mask ? mask_count[0] : (unsigned long long)N;
+    count[0] = c;
+    inv_count[0] = c > 0 ? (float)(1.0 / (double)c) : 0.f;
+  }
+}
+
+hipError_t launch_count_prep(const unsigned long long *mask_count, bool has_mask, int64_t N,
+                             unsigned long long *count, float *inv_count, hipStream_t s) {
+  hipLaunchKernelGGL(k_count_prep, dim3(1), dim3(64), 0, s, mask_count, has_mask ? 1 : 0,
+                     (long long)N, count, inv_count);
+  return hipGetLastError();
+}
+
+// status[0] = bad_code if the validation scan raised its flag, else 0.
+__global__ void k_status_out(const int *flags, int bad_code, int32_t *status) {
+  if (threadIdx.x == 0) status[0] = flags[0] ? bad_code : 0;
+}
+
+hipError_t launch_status_out(const int *flags, int32_t bad_code, int32_t *status, hipStream_t s) {
+  hipLaunchKernelGGL(k_status_out, dim3(1), dim3(64), 0, s, flags, (int)bad_code, status);
   return hipGetLastError();
 }
 
@@ -1971,7 +2007,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigned short *dzt,
                                                  long long tst, const int32_t *idx,
                                                  const float *p, const float *srow, int rows,
-                                                 int K) {
+                                                 int K, int vlim) {
   __shared__ int tab[4][kScatTab];
   const int w = threadIdx.x >> 6;
   const int r = blockIdx.x * 4 + w, lane = threadIdx.x & 63;
@@ -1980,13 +2016,14 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigne
   if (sr == 0.f) return;
   const int32_t *ir = idx + (long long)r * K;
   const float *pr = p + (long long)r * K;
-  // repeated index test (a negative index lies outside this vocabulary shard: skipped)
+  // repeated index test; an index outside [0, vlim) is skipped everywhere (negative: outside
+  // this vocabulary shard; vlim or more: an invalid entry that the validation scan reports)
   bool dup = K > kScatTab / 2;
   if (!dup) {
     for (int i = lane; i < kScatTab; i += 64) tab[w][i] = -1;
     for (int k = lane; k < K; k += 64) {
       const int v = ir[k];
-      if (v < 0) continue;
+      if ((unsigned)v >= (unsigned)vlim) continue;
       unsigned hs = ((unsigned)v * 2654435761u) >> 23;  // 9 bits
       for (int probe = 0; probe < kScatTab; ++probe) {  // a free slot always exists
         const int old = atomicCAS(&tab[w][hs], -1, v);
@@ -2003,7 +2040,7 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigne
   if (!dup) {
     for (int k = lane; k < K; k += 64) {
       const int v = ir[k];
-      if (v >= 0) scatter_one<DT>(dz, ts, dzt, tst, r, v, sr * pr[k]);
+      if ((unsigned)v < (unsigned)vlim) scatter_one<DT>(dz, ts, dzt, tst, r, v, sr * pr[k]);
     }
     return;
   }
@@ -2012,7 +2049,7 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigne
     const bool has = k < K;
     const int v = has ? ir[k] : -1;
     float tot = has ? pr[k] : 0.f;
-    bool first = has && v >= 0;
+    bool first = has && (unsigned)v < (unsigned)vlim;
     for (int j0 = 0; j0 < K; j0 += 64) {
       const int jl = j0 + lane;
       const int vjl = jl < K ? ir[jl] : -1;
@@ -2034,15 +2071,16 @@ __global__ __launch_bounds__(256) void k_scatter(void *dz, long long ts, unsigne
 
 hipError_t launch_scatter(int dtype, void *dz, void *dzt, int64_t tst, int64_t C_alloc,
                           const int32_t *idx_c, const float *p_c, const float *srow, int64_t rows,
-                          int32_t K, hipStream_t s) {
+                          int32_t K, int64_t V_pad, hipStream_t s) {
   const int blocks = (int)((rows + 3) / 4);
   if (dtype == 1)
     hipLaunchKernelGGL(k_scatter<1>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256,
                        (unsigned short *)dzt, (long long)tst, idx_c, p_c, srow, (int)rows,
-                       (int)K);
+                       (int)K, (int)V_pad);
   else
     hipLaunchKernelGGL(k_scatter<0>, dim3(blocks), dim3(256), 0, s, dz, (long long)C_alloc * 256,
-                       (unsigned short *)nullptr, 0LL, idx_c, p_c, srow, (int)rows, (int)K);
+                       (unsigned short *)nullptr, 0LL, idx_c, p_c, srow, (int)rows, (int)K,
+                       (int)V_pad);
   return hipGetLastError();
 }
 

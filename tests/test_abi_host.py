@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_profile_classes(lib):
-    assert lib.kd_version() == 4
+    assert lib.kd_version() == 5
     names = kd.profile_classes()
     assert "fwd_gemm_lse" in names and "dw_gemm" in names and len(names) == len(set(names))
 
@@ -343,3 +343,13 @@ def test_clock_stamp_rejects_bad_arguments_before_any_gpu_work(lib):
     assert lib.kd_clock_stamp(0x1000, 0, None) == E_ARG
     assert lib.kd_clock_stamp(0x1000, 65537, None) == E_ARG
     assert lib.kd_wall_clock_khz(None) == E_ARG
+
+
+def test_async_call_requires_an_aligned_status_before_any_gpu_work(lib):
+    """kd_chunked_kl_fwd_bwd_async checks its status pointer on the host first: a missing
+    or misaligned one returns KD_E_ARG without touching a device."""
+    args = [0x1000, 0x2000, 1, 0x3000, 0x4000, None, 64, 64, 100, 4, 32,
+            0x5000, 0x6000, 0x7000, None, None, None]
+    assert lib.kd_chunked_kl_fwd_bwd_async(*args, None, 0x8000, 1 << 20, None) == E_ARG
+    assert lib.kd_last_error()
+    assert lib.kd_chunked_kl_fwd_bwd_async(*args, 0x9002, 0x8000, 1 << 20, None) == E_ARG
