@@ -161,7 +161,8 @@ int kd_chunked_kl_fwd_bwd(const void *h, const void *W, int32_t dtype,
  * KD_E_HIP for a failed launch.  Every device operation is a kernel launch on `stream`
  * (no memset or copy), and the sequence depends only on the sizes, the pointers and the
  * workspace size, so a recorded graph replays it for new contents of the same buffers.
- * The kernel timing of kd_profile_enable must be off while recording.
+ * The kernel timing of kd_profile_enable must be off while recording, and one ordinary
+ * call should come first, so that loading the kernels is not part of the recording.
  */
 int kd_chunked_kl_fwd_bwd_async(const void *h, const void *W, int32_t dtype,
                                 const int32_t *topk_idx, const float *topk_p,
